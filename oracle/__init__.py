@@ -1,0 +1,114 @@
+"""Oracle for the attention forward pass: plain, slow, obviously correct, fp64, CPU.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this package. The product path (the HIP
+library and its Python binding) never imports, links or calls anything here,
+and nothing here imports the product path.
+
+Two parts:
+
+* ``attention`` -- standard attention by its definition (``attention.c``):
+  "Writing a FlashAttention kernel in Metal", section "Standard attention", with
+  the causal rule of its section "Blockwise attention and causal masking", and L
+  as defined in "FlashAttention-2 from PyTorch to Triton", section "What We Are
+  Building".
+* ``blockwise`` -- fp64 models of the pages' online-softmax recurrences (the
+  method itself), used by the tests to tie the recurrence to the definition.
+
+Pins: every function here is checked, in ``tests/test_oracle.py`` and
+``tests/test_blockwise.py``, against closed forms, invariants, brute force on
+tiny inputs, torch's own scaled-dot-product attention in fp64 and the worked
+two-block example of the first page's "Online softmax" section.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attention.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``attention.c`` into ``liboracle.so`` with gcc (no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-o", _LIB_PATH, _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return _LIB_PATH
+
+
+def load_library(path: str):
+    """Open a compiled copy of ``attention.c`` and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_attention_f64.restype = ctypes.c_int
+    lib.oracle_attention_f64.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int64,
+    ]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on (all host cores unless OMP_NUM_THREADS says otherwise)."""
+    return int(_load().oracle_num_threads())
+
+
+def attention(Q, K, V, causal: bool, scale: float, rows=None, lib=None):
+    """Standard attention in fp64.
+
+    Q, K, V: array-likes of shape [B, H, N, d] (or [N, d], treated as B=H=1),
+    up-cast losslessly to fp64. ``scale`` multiplies the scores as given.
+    ``rows``: None for every query row, else a 1-D list of query indices.
+
+    Returns (O, L) as fp64 numpy arrays: O [B, H, R, d], L [B, H, R] with R = N
+    or len(rows) (squeezed back to [R, d] / [R] for 2-D input).
+    ``lib`` selects another compiled copy (from ``load_library``); default: this one.
+    """
+    lib = lib or _load()
+    q = np.ascontiguousarray(np.asarray(Q, dtype=np.float64))
+    k = np.ascontiguousarray(np.asarray(K, dtype=np.float64))
+    v = np.ascontiguousarray(np.asarray(V, dtype=np.float64))
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"expected equal [B,H,N,d] shapes, got {q.shape} {k.shape} {v.shape}")
+    B, H, N, d = q.shape
+    if rows is None:
+        idx = None
+        R = N
+        rows_ptr = None
+    else:
+        idx = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+        R = int(idx.size)
+        rows_ptr = idx.ctypes.data
+    O = np.empty((B, H, R, d), dtype=np.float64)
+    L = np.empty((B, H, R), dtype=np.float64)
+    st = lib.oracle_attention_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                  O.ctypes.data, L.ctypes.data, B, H, N, d,
+                                  1 if causal else 0, float(scale), rows_ptr, R)
+    if st != 0:
+        raise RuntimeError(f"oracle_attention_f64 failed with status {st}")
+    if squeeze:
+        return O[0, 0], L[0, 0]
+    return O, L
