@@ -1,0 +1,189 @@
+"""Throughput of the attention forward pass on one MI355X.
+
+One step = one fa_fwd call over the whole workload (all heads, all query tiles) with
+Q, K, V, O, L resident in HBM. Default workload: causal bf16, B=4, H=16, N=4096,
+d=128. Prints one JSON line. ``value`` is algorithmic TFLOP/s: 4 d FLOP per
+admissible (query, key) pair -- 2d for the score, 2d for the weighted value row --
+with N(N+1)/2 pairs per head when causal.
+
+The roofline object compares the kernel against the MI355X published dense bf16
+MFMA peak; ``traffic`` is the HBM traffic measured by rocprofv3 counters for the
+same kernel source (null when the kernel source has changed since). The CPU
+baseline times the fp64 oracle on a bounded sample of query rows on the host cores
+(on the GPU machine), and checks the sampled rows of the GPU output against it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16, causal, B4 H16 N4096 d128)"
+# MI355X published dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU;
+# fp32 matrix 157.3.
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+KERNEL_SOURCE = os.path.join(ROOT, "tiled_online_softmax_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("source_sha256") != source_digest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, O, L, target_s: float):
+    """Time the oracle on evenly spaced query rows of every head; check those rows."""
+    import numpy as np
+
+    import oracle
+
+    qn, kn, vn = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    heads = w.B * w.H
+
+    def run(nrows):
+        rows = np.unique(np.linspace(0, w.N - 1, nrows).round().astype(np.int64))
+        t0 = time.perf_counter()
+        Oref, Lref = oracle.attention(qn, kn, vn, w.causal, w.scale, rows=rows)
+        return rows, Oref, Lref, time.perf_counter() - t0
+
+    rows, Oref, Lref, t = run(8)
+    nrows = int(min(w.N, max(8, 8 * target_s / max(t, 1e-3))))
+    if nrows > 8:
+        rows, Oref, Lref, t = run(nrows)
+    pairs = (rows + 1).sum() if w.causal else len(rows) * w.N
+    flops = 4.0 * w.d * float(pairs) * heads
+    o = O.double().cpu().numpy()[:, :, rows]
+    l = L.double().cpu().numpy()[:, :, rows]
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{len(rows)} evenly spaced query rows of each of the {heads} heads "
+                  f"(full rows of S and P in fp64), {t:.1f} s",
+        "seconds": t,
+        "sampled_rows_max_abs_err": {"O": float(np.max(np.abs(o - Oref))),
+                                     "L": float(np.max(np.abs(l - Lref)))},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the causal bf16 B4 H16 N4096 d128)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(heads are independent: each GPU would run this kernel on its share).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_online_softmax_amd as fa
+    from workloads import HEADLINE, WORKLOADS
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    q, k, v = w.make()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    O = torch.empty_like(qd)
+    L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_fwd(qd, kd, vd, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: HIP events on the stream the kernel is enqueued on.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for (a, b) in per:
+        a.record(stream)
+        step()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    launch_ms = sorted(a.elapsed_time(b) for (a, b) in per)
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(w.name)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs, cast to the workload dtype)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_ms": {"avg": round(avg_launch_ms, 5), "median": round(launch_ms[len(launch_ms) // 2], 5),
+                          "min": round(launch_ms[0], 5), "max": round(launch_ms[-1], 5)},
+            "algorithmic_flop_per_launch": flops,
+            "algorithmic_bytes_per_launch": w.io_bytes(),
+        },
+        "wall_s_timed": round(t_wall, 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, O, L, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

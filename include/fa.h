@@ -1,0 +1,82 @@
+/*
+ * fa.h -- C ABI of the tiled online-softmax attention forward pass (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention with the per-row
+ * logsumexp, as defined in "Writing a FlashAttention kernel in Metal"
+ * (section "Standard attention": S = scale * Q K^T, P = row softmax of S,
+ * O = P V; section "Blockwise attention and causal masking": with causal
+ * masking a query attends only to keys at or before its own position) and in
+ * "FlashAttention-2 from PyTorch to Triton" (section "What We Are Building":
+ * L_i = m_i + log l_i, the natural-log logsumexp of row i of the scaled
+ * scores). It is computed by the tiled online-softmax recurrence (running row
+ * maximum, running row sum and an unnormalised output accumulator, divided by
+ * the sum once at the end), so the N x N score matrix is never stored.
+ *
+ * This header is plain C. It needs no HIP or torch header.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. FA_OK is zero; every other value is an error. */
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, B/H/N < 1, scale not finite or <= 0, bad dtype */
+  FA_ERR_UNSUPPORTED = 2,      /* head dimension d other than 64 or 128, or a size too large */
+  FA_ERR_MISALIGNED = 3,       /* a buffer not 16-byte aligned */
+  FA_ERR_LAUNCH = 4            /* the HIP runtime refused the kernel launch */
+} fa_status_t;
+
+/* Element type of Q, K, V and O. */
+typedef enum {
+  FA_DTYPE_F32 = 0, /* IEEE binary32; all arithmetic in fp32 */
+  FA_DTYPE_BF16 = 1 /* bfloat16 inputs and output; fp32 scores, softmax state and accumulation */
+} fa_dtype_t;
+
+/*
+ * fa_fwd -- attention forward pass over B*H independent heads.
+ *
+ *   Q, K, V  device pointers, contiguous row-major [B][H][N][d] of `dtype`.
+ *   O        device pointer, contiguous [B][H][N][d] of `dtype`; written.
+ *            O[b][h][i][:] = sum_j P[i][j] V[b][h][j][:], rounded to nearest
+ *            even when dtype is bf16. Must not overlap Q, K, V or L.
+ *   L        device pointer, contiguous [B][H][N] fp32; written with the
+ *            natural-log logsumexp of each row of scaled scores.
+ *   B, H, N  batch, heads, sequence length (queries and keys share positions
+ *            0..N-1). Each >= 1. N need not be a multiple of any tile size.
+ *   d        head dimension: 64 or 128.
+ *   causal   0: every query sees every key. Non-zero: query i sees keys j <= i.
+ *   scale    multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
+ *   stream   hipStream_t to enqueue on (NULL = the null stream).
+ *   dtype    an fa_dtype_t value.
+ *
+ * Ownership: the caller owns all five buffers; the library allocates no
+ * memory and keeps no state between calls. The call is asynchronous: it
+ * returns once the kernel is enqueued, and the results are valid after the
+ * caller synchronises the stream. Arguments are validated synchronously,
+ * before any device work, in the order of the status list above; on an error
+ * nothing is enqueued and O, L are untouched. Faults inside the kernel (for
+ * example a pointer that is not device memory) surface at the caller's next
+ * synchronisation, not here. Calls on different streams may run
+ * concurrently; they share no state.
+ */
+fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void *O, float *L,
+                   int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                   void *stream, int dtype);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *fa_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

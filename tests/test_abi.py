@@ -1,0 +1,88 @@
+"""The C ABI: the library loads without a GPU, exports what include/fa.h declares,
+and rejects bad arguments synchronously, before any device work (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+fa = pytest.importorskip("tiled_online_softmax_amd", reason="libfa.so not built")
+
+A = 1 << 20  # fake, 16-byte aligned "device" addresses: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_fwd", "fa_status_string", "fa_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_strings_and_version():
+    assert fa.fa_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert fa.fa_status_string(s) not in ("ok", "unknown status")
+    assert fa.fa_status_string(99) == "unknown status"
+    assert fa.fa_version() >= 100
+
+
+def call(Q=A, K=2 * A, V=3 * A, O=4 * A, L=5 * A, B=1, H=1, N=64, d=64, causal=0, scale=0.125,
+         dtype=fa.FA_DTYPE_BF16):
+    return fa.raw_fa_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, None, dtype)
+
+
+@pytest.mark.parametrize("kw", [dict(Q=0), dict(K=0), dict(V=0), dict(O=0), dict(L=0)])
+def test_null_pointer(kw):
+    assert call(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=-5), dict(B=-1)])
+def test_bad_sizes(kw):
+    assert call(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan")])
+def test_bad_scale(scale):
+    assert call(scale=scale) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_bad_dtype():
+    assert call(dtype=7) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("d", [16, 32, 63, 96, 256])
+def test_unsupported_head_dim(d):
+    assert call(d=d) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_too_long_sequence():
+    assert call(N=(1 << 24) + 1) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_overlapping_output():
+    # O overlaps K
+    assert call(O=2 * A + 64) == fa.FA_ERR_INVALID_ARGUMENT
+    # L overlaps O
+    assert call(L=4 * A + 16) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(Q=A + 8), dict(V=3 * A + 2), dict(L=5 * A + 4)])
+def test_misaligned(kw):
+    assert call(**kw) == fa.FA_ERR_MISALIGNED
+
+
+def test_validation_order_null_before_unsupported():
+    assert call(Q=0, d=96) == fa.FA_ERR_INVALID_ARGUMENT

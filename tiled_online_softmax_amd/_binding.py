@@ -1,0 +1,106 @@
+"""ctypes binding of libfa.so: argument marshalling only.
+
+Every step of the attention forward pass runs in the HIP kernels of libfa.so; this
+module checks tensor metadata, passes raw device pointers, sizes and the stream
+handle, and turns status codes into exceptions. There is no fallback: if the
+library is missing, importing the package fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARGUMENT = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_MISALIGNED = 3
+FA_ERR_LAUNCH = 4
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_lib.fa_fwd.restype = ctypes.c_int
+_lib.fa_fwd.argtypes = [
+    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+    ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+]
+_lib.fa_status_string.restype = ctypes.c_char_p
+_lib.fa_status_string.argtypes = [ctypes.c_int]
+_lib.fa_version.restype = ctypes.c_int
+_lib.fa_version.argtypes = []
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"fa_fwd failed: {fa_status_string(status)} (status {status})")
+        self.status = status
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return int(_lib.fa_version())
+
+
+def raw_fa_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """The C entry point with integer pointers; returns the status code."""
+    return int(_lib.fa_fwd(Q, K, V, O, L, B, H, N, d, int(causal), float(scale), stream, int(dtype)))
+
+
+_DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
+
+
+def _ptr(t):
+    return t.data_ptr() if isinstance(t, torch.Tensor) else int(t)
+
+
+def fa_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, stream=None):
+    """Enqueue the forward pass on ``stream`` (default: torch's current stream).
+
+    Q, K, V, O: contiguous [B, H, N, d] device tensors of one dtype (bf16 or fp32);
+    L: contiguous [B, H, N] fp32 device tensor. Raises FaError on a bad argument.
+    """
+    tensors = (Q, K, V, O)
+    dt = Q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for t in tensors:
+        if t.dtype != dt or tuple(t.shape) != (B, H, N, d) or not t.is_contiguous():
+            raise ValueError("Q, K, V, O must be contiguous [B, H, N, d] tensors of one dtype")
+        if t.device.type != "cuda" or t.device != Q.device:
+            raise ValueError("all tensors must live on the same GPU")
+    if L.dtype != torch.float32 or tuple(L.shape) != (B, H, N) or not L.is_contiguous() or L.device != Q.device:
+        raise ValueError("L must be a contiguous fp32 [B, H, N] tensor on the same GPU")
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    st = raw_fa_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, N, d, causal, scale,
+                    stream, _DTYPES[dt])
+    if st != FA_OK:
+        raise FaError(st)
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate O (like q) and fp32 L, run fa_fwd, return (O, L)."""
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32).item())
+    O = torch.empty_like(q)
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, O, L, B, H, N, d, causal, scale, stream)
+    return O, L
