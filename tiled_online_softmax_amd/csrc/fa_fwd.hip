@@ -40,6 +40,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 
 namespace {
@@ -92,20 +94,98 @@ __device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bo
 // ---------------------------------------------------------------------------
 // bf16 kernel: Q, K, V, O bf16; S, P, m, l, O accumulation fp32; P rounded to
 // bf16 (the element type of V) only as the operand of the second MFMA.
+//
+// LDS: two stages, each holding one K tile and one V tile of BN keys. Tiles are
+// written by buffer_load_dwordx4 ... lds (global -> LDS without VGPRs, 1 KiB
+// per wave instruction, lane l writing bytes [16l, 16l+16)); rows past N read
+// as zero through the buffer range check. Inside a row the 16-byte chunks are
+// XOR-permuted so that both read patterns are free of bank conflicts:
+//  * K (ds_read_b128, lanes = 32 consecutive keys, same chunk): chunk c of
+//    row r sits in slot c ^ swz_k(r), with swz_k spreading 16 consecutive rows
+//    over the 16 slots of a 256-byte bank line;
+//  * V (ds_read_b64_tr_b16, a 16-lane group reads 4 consecutive rows x 32
+//    bytes and its partner group the next 32 bytes): slot c ^ swz_v(r) with
+//    swz_v(r) = 4 * (row index within the group of 4) so the 4 x 4 chunks of
+//    a group pair land in 16 distinct slots.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
+template <int D, int BN, int NW>
+struct BfLayout {
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int RPB = 16 / CPR;             // rows per 256-byte bank line
+  static constexpr int ROW = D * 2;                // bytes per row
+  static constexpr int TILE = BN * ROW;            // bytes per K (or V) tile
+  static constexpr int STAGE = 2 * TILE;           // K tile then V tile
+  static constexpr int LOADS = TILE / 1024;        // wave instructions per tile matrix
+  static constexpr int LPW = LOADS / NW;           // ... per wave
+  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+  static_assert(BN % 32 == 0, "key tile is a multiple of the 32-key MFMA block");
+  __device__ static constexpr int swz_k(int r) { return (r / RPB) & (CPR - 1); }
+  __device__ static constexpr int swz_v(int r) { return 4 * ((r / RPB) & (4 / RPB - 1)); }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+
+// ds_read_b64_tr_b16 issued as inline assembly. Through the builtin, the
+// compiler cannot tell these LDS reads from the asynchronous global->LDS loads
+// of the next tile (into the other stage) and waits for those loads to land
+// first; here it does not see an LDS access at all. The result must therefore
+// be released by lds_wait_all before use.
+__device__ __forceinline__ v2u32 ds_read_tr16_b64(uint32_t addr) {
+  v2u32 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// Wait for all outstanding LDS reads; the registers passed through the asm tie
+// every later use of them to this wait.
+template <int N>
+__device__ __forceinline__ void lds_wait_all(v2u32 (&v)[N][2]) {
+  if constexpr (N == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]));
+  } else {
+    static_assert(N == 4, "two or four 32-column blocks");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]),
+                   "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1]));
+  }
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled; reads past the
+// end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voffset into LDS
+// at `lds` + 16 * lane. The builtin exists only for the GPU target, and the
+// host compilation pass of a kernel template that names it drops the kernel's
+// launch stub, so it is compiled for the device pass alone (this function has
+// no host caller).
+__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds, 16, voffset, 0, 0, 0);
+#endif
+}
+
+// Rows of a reference maximum may lag the true running maximum by up to this
+// much (base-2 exponent) before the accumulators are rescaled: weights stay
+// below 2^8, and O/l and m + log2 l do not depend on the reference chosen.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, bool CAUSAL, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     bf16 *__restrict__ O, float *__restrict__ L, int N, int n_qtiles, float c) {
-  constexpr int BN = 64;               // keys per LDS tile
-  constexpr int KS = D + 8;            // K row stride in LDS (elements): 16 B pad
-  constexpr int VS = D + 32;           // V row stride in LDS (elements): 64 B pad
-  constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int PER_T = BN * CPR / kThreads;  // chunks of K (and of V) per thread
-  static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
-
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BN * VS];
+  using LY = BfLayout<D, BN, NW>;
+  constexpr int BM = kRowsPerWave * NW;  // query rows per workgroup
+  constexpr int NKB = BN / 32;           // 32-key MFMA blocks per tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * LY::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
@@ -118,11 +198,47 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
   const bf16 *Kh = K + head;
   const bf16 *Vh = V + head;
 
-  const int q0 = qt * kBlockM;
+  const int q0 = qt * BM;
   const int qw = q0 + kRowsPerWave * wave;  // first query row of this wave
   const int qrow = qw + l32;                // the query row this lane carries
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16c + 8hh + 0..7].
+  // Per-lane byte offsets (within a tile) of this wave's share of the tile loads:
+  // LDS slot p = 1024 * gi + 16 * lane holds chunk (slot ^ swz(row)) of row p / ROW.
+  int kvo[LY::LPW], vvo[LY::LPW];
+#pragma unroll
+  for (int i = 0; i < LY::LPW; ++i) {
+    const int p = 64 * (wave * LY::LPW + i) + lane;  // 16-byte slot index in the tile
+    const int r = p / LY::CPR, j = p % LY::CPR;
+    kvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_k(r));
+    vvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_v(r));
+  }
+  auto issue = [&](int t, int stage) {
+    const int k0 = t * BN;
+    const int bytes = (N - k0) * LY::ROW;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + (size_t)k0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vh + (size_t)k0 * D, bytes);
+    char *kdst = smem + stage * LY::STAGE;
+#pragma unroll
+    for (int i = 0; i < LY::LPW; ++i) {
+      const int gi = wave * LY::LPW + i;
+      load_lds_16(kr, kdst + 1024 * gi, kvo[i]);
+      load_lds_16(vr, kdst + LY::TILE + 1024 * gi, vvo[i]);
+    }
+  };
+
+  // K reads (A operand of S^T = K Q^T): row 32kb + l32, chunk 2cc + hh.
+  // The chunk index only flips bits 5..7 of the byte address, so a per-cc XOR
+  // of one base address gives every step.
+  const int krow = l32;
+  const int kbase = krow * LY::ROW + 16 * (hh ^ LY::swz_k(krow));
+  // V transposing reads: 16-lane group g reads rows 4hh + (lane%16)/4 (+8u, +16mm,
+  // +32kb) and columns 32db + 16(g%2) + 4(lane%4); in slot terms the column block
+  // db is XORed with swz_v(row)/4.
+  const int vrow = 4 * hh + (lane % 16) / 4;
+  const int vchunk = 2 * ((lane / 16) % 2) + (lane % 4) / 2;  // chunk within a 32-column block
+  const int vbase = vrow * LY::ROW + 16 * (vchunk ^ LY::swz_v(vrow)) + 8 * (lane % 2);
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16cc + 8hh + 0..7].
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int cc = 0; cc < D / 16; ++cc) {
@@ -135,71 +251,39 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m = -INFINITY;  // running row maximum, base-2 scaled domain
-  float lsum = 0.f;     // running row sum over this half-wave's keys
+  float m = -INFINITY;  // reference row maximum (base-2 scaled domain)
+  float lsum = 0.f;     // row sum relative to m over this half-wave's keys
 
-  const int kend = CAUSAL ? min(N, q0 + kBlockM) : N;
+  const int kend = CAUSAL ? min(N, q0 + BM) : N;
   const int ntiles = (kend + BN - 1) / BN;
+  // Leading tiles that need no mask for any row of the workgroup.
+  const int nfull = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
 
-  // Global -> register staging of one K/V tile (contiguous rows of the head).
-  u32x4 kr[PER_T], vr[PER_T];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      const int key = t * BN + row;
-      if (key < N) {
-        kr[i] = *(const u32x4 *)(Kh + (size_t)key * D + 8 * ch);
-        vr[i] = *(const u32x4 *)(Vh + (size_t)key * D + 8 * ch);
-      } else {  // ragged end: zero rows (their scores are masked as well)
-        kr[i] = u32x4{};
-        vr[i] = u32x4{};
-      }
-    }
-  };
-  auto swrite = [&]() {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      *(u32x4 *)(&Ks[row * KS + 8 * ch]) = kr[i];
-      *(u32x4 *)(&Vs[row * VS + 8 * ch]) = vr[i];
-    }
-  };
-
-  gload(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done reading the previous tile
-    swrite();
-    __syncthreads();  // the tile is complete in LDS
-    if (t + 1 < ntiles) gload(t + 1);
-
-    if (qw >= N) continue;  // wave past the ragged end: loads and barriers only
+  auto compute = [&](int t, int stage, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int k0 = t * BN;
+    if (EDGE && CAUSAL && k0 > qw + kRowsPerWave - 1) return;  // wholly after this wave's rows
+    const char *ks = smem + stage * LY::STAGE;
+    const char *vs = ks + LY::TILE;
 
-    // S^T blocks of 32 keys x 32 queries. Result layout: lane (l32, hh),
-    // register r holds key 8(r/4) + 4hh + r%4 of the block, query qrow.
-    f32x16 s[2];
-    bool act[2];
+    f32x16 s[NKB];
+    bool act[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       const int kb0 = k0 + 32 * kb;
-      act[kb] = kb0 < N && (!CAUSAL || kb0 <= qw + kRowsPerWave - 1);
-      s[kb] = f32x16{};
+      act[kb] = !EDGE || ((kb0 < N) && (!CAUSAL || kb0 <= qw + kRowsPerWave - 1));
       if (act[kb]) {
 #pragma unroll
         for (int cc = 0; cc < D / 16; ++cc) {
-          // A operand: K[kb0 + l32][16cc + 8hh + 0..7]
-          const bf16x8 a = *(const bf16x8 *)(&Ks[(32 * kb + l32) * KS + 16 * cc + 8 * hh]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], s[kb], 0, 0, 0);
+          const bf16x8 a = *(const bf16x8 *)(ks + 32 * kb * LY::ROW + (kbase ^ (32 * cc)));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc == 0 ? f32x16{} : s[kb], 0, 0, 0);
         }
-        const bool edge = (kb0 + 31 >= N) || (CAUSAL && kb0 + 31 > qw);
-        if (edge) {
+        if (EDGE) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kb0 + 8 * (r / 4) + 4 * hh + (r % 4);
-            if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+            const bool bad = key >= N || (CAUSAL && key > qrow);
+            s[kb][r] = bad ? -INFINITY : s[kb][r];
           }
         }
       } else {
@@ -208,61 +292,85 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_bf16_kernel(
       }
     }
 
-    // Row maximum over the tile, then the online-softmax update.
+    // Row maximum of the tile (16 keys per lane per block, then the partner half).
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = halves_max(mx);
-    const float m_new = fmaxf(m, mx * c);
-    // Guard: a row with no admissible key so far keeps a zero reference so
-    // that no -inf - -inf appears (such rows have l == 0 and O == 0).
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m - m_ref);
-    m = m_new;
+    const float mc = mx * c;
+    // Move the reference maximum only when some row of the wave grew past the
+    // slack; rows that did not grow get alpha = 1.
+    const bool grow = mc > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mc : m;
+      const float alpha = exp2_fast(m - m_new);  // 0 while m is still -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = m_new;
+    }
+    const float mref = (m == -INFINITY) ? 0.f : m;
 
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kb][r], c, -m_ref));
+        const float p = exp2_fast(fmaf(s[kb][r], c, -mref));
         s[kb][r] = p;
         psum += p;
       }
-    lsum = fmaf(alpha, lsum, psum);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    lsum += psum;
 
-    // O^T += V^T P^T. B operand (P^T, keys x queries) for key half mm of
-    // block kb is registers 8mm..8mm+7 of s[kb], i.e. keys
-    // 16mm + 8(t/4) + 4hh + t%4 for slot t; the A operand (V^T, d x keys)
-    // must list the same keys: two transposing reads of 4 consecutive keys.
+    // O^T += V^T P^T. B operand (P^T) for key half mm of block kb is registers
+    // 8mm..8mm+7 of s[kb] (keys 16mm + 8(t/4) + 4hh + t%4 for slot t); the A
+    // operand (V^T) lists the same keys via two transposing reads of 4 keys.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       if (!act[kb]) continue;
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
         bf16x8 pb;
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) pb[t8] = (bf16)s[kb][8 * mm + t8];
-        const int vrow = 32 * kb + 16 * mm + 4 * hh + (lane % 16) / 4;
-        const int vcol = 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+        const int roff = (32 * kb + 16 * mm) * LY::ROW;
+        // All transposing reads of this key half first, then one LDS wait whose
+        // register operands order the MFMAs after it.
+        v2u32 vt[D / 32][2];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16 *p0 = &Vs[vrow * VS + 32 * db + vcol];
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0 + 8 * VS));
+          const uint32_t a0 = lds_addr(vs + roff + (vbase ^ (64 * db)));
+          vt[db][0] = ds_read_tr16_b64(a0);
+          vt[db][1] = ds_read_tr16_b64(a0 + 8 * LY::ROW);
+        }
+        lds_wait_all(vt);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
           const bf16x8 a = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              bf16x8, __builtin_shufflevector(vt[db][0], vt[db][1], 0, 1, 2, 3));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
         }
       }
     }
-  }
+  };
+
+  // One barrier per tile: after it, every wave's share of tile t is in LDS and
+  // every wave has finished reading the other stage, which the loads of tile
+  // t+1 then overwrite while tile t is computed.
+  auto step = [&](int t, auto edge_tag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    if (qw < N) compute(t, t & 1, edge_tag);
+  };
+  issue(0, 0);
+  int t = 0;
+  for (; t < nfull; ++t) step(t, std::false_type{});
+  for (; t < ntiles; ++t) step(t, std::true_type{});
 
   if (qw >= N) return;
   // Epilogue: one division by the row sum (both half-waves' keys), RNE to bf16.
@@ -443,12 +551,40 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_f32_kernel(
   }
 }
 
-template <typename Kern>
-hipError_t launch(Kern kern, int nblocks, hipStream_t stream, const void *Q, const void *K,
-                  const void *V, void *O, float *L, int N, int n_qtiles, float c) {
+hipError_t launch(const void *kern, int nblocks, int threads, hipStream_t stream, const void *Q,
+                  const void *K, const void *V, void *O, float *L, int N, int n_qtiles, float c) {
   void *args[] = {(void *)&Q, (void *)&K, (void *)&V, (void *)&O,
                   (void *)&L, (void *)&N, (void *)&n_qtiles, (void *)&c};
-  return hipLaunchKernel((const void *)kern, dim3(nblocks), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(kern, dim3(nblocks), dim3(threads), args, 0, stream);
+}
+
+// Tile configuration of the bf16 kernel: waves per workgroup (32 query rows
+// each) and keys per LDS tile.
+#ifndef FA_BF16_NW
+#define FA_BF16_NW 4
+#endif
+#ifndef FA_BF16_BN
+#define FA_BF16_BN 64
+#endif
+constexpr int kBf16Waves = FA_BF16_NW;
+constexpr int kBf16Keys = FA_BF16_BN;
+
+template <int D, bool CAUSAL>
+hipError_t launch_bf16(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
+                       const void *V, void *O, float *L, float c) {
+  constexpr int BM = kRowsPerWave * kBf16Waves;
+  const int nq = (N + BM - 1) / BM;
+  const void *kern = (const void *)&fa_fwd_bf16_kernel<D, CAUSAL, kBf16Waves, kBf16Keys>;
+  return launch(kern, (int)(BH * nq),
+                64 * kBf16Waves, s, Q, K, V, O, L, N, nq, c);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_f32(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
+                      const void *V, void *O, float *L, float c) {
+  const int nq = (N + kBlockM - 1) / kBlockM;
+  const void *kern = (const void *)&fa_fwd_f32_kernel<D, CAUSAL>;
+  return launch(kern, (int)(BH * nq), kThreads, s, Q, K, V, O, L, N, nq, c);
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -481,25 +617,25 @@ extern "C" fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void 
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)L) & 15)
     return FA_ERR_MISALIGNED;
 
-  const int nblocks = (int)(B * H * n_qtiles);
   const float c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   hipStream_t s = (hipStream_t)stream;
-  const int n = (int)N, nq = (int)n_qtiles;
+  const int n = (int)N;
+  const int64_t BH = B * H;
   hipError_t err;
   if (dtype == FA_DTYPE_BF16) {
     if (d == 64)
-      err = causal ? launch(fa_fwd_bf16_kernel<64, true>, nblocks, s, Q, K, V, O, L, n, nq, c)
-                   : launch(fa_fwd_bf16_kernel<64, false>, nblocks, s, Q, K, V, O, L, n, nq, c);
+      err = causal ? launch_bf16<64, true>(BH, n, s, Q, K, V, O, L, c)
+                   : launch_bf16<64, false>(BH, n, s, Q, K, V, O, L, c);
     else
-      err = causal ? launch(fa_fwd_bf16_kernel<128, true>, nblocks, s, Q, K, V, O, L, n, nq, c)
-                   : launch(fa_fwd_bf16_kernel<128, false>, nblocks, s, Q, K, V, O, L, n, nq, c);
+      err = causal ? launch_bf16<128, true>(BH, n, s, Q, K, V, O, L, c)
+                   : launch_bf16<128, false>(BH, n, s, Q, K, V, O, L, c);
   } else {
     if (d == 64)
-      err = causal ? launch(fa_fwd_f32_kernel<64, true>, nblocks, s, Q, K, V, O, L, n, nq, c)
-                   : launch(fa_fwd_f32_kernel<64, false>, nblocks, s, Q, K, V, O, L, n, nq, c);
+      err = causal ? launch_f32<64, true>(BH, n, s, Q, K, V, O, L, c)
+                   : launch_f32<64, false>(BH, n, s, Q, K, V, O, L, c);
     else
-      err = causal ? launch(fa_fwd_f32_kernel<128, true>, nblocks, s, Q, K, V, O, L, n, nq, c)
-                   : launch(fa_fwd_f32_kernel<128, false>, nblocks, s, Q, K, V, O, L, n, nq, c);
+      err = causal ? launch_f32<128, true>(BH, n, s, Q, K, V, O, L, c)
+                   : launch_f32<128, false>(BH, n, s, Q, K, V, O, L, c);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
