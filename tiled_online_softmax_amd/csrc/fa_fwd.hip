@@ -75,19 +75,27 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Workgroup index -> (head, query tile). Workgroups are dispatched to XCDs
-// round-robin (bid % 8); renumber them so each XCD receives one contiguous
-// run of the logical order, in its own dispatch order. The logical order is
-// head-major; for causal attention query tiles run from the last (most key
-// tiles) to the first within each head.
+// Workgroup index -> (head, query tile). Workgroups are dispatched to the
+// eight XCDs round-robin (XCD = bid % 8, in order bid / 8 within an XCD).
+// When the heads split evenly over the XCDs, XCD x takes heads
+// [x*hpx, (x+1)*hpx), so each head's K/V stays in one XCD's L2; within an XCD,
+// and globally otherwise, work is ordered by query tile, all heads at one
+// tile before the next. For causal attention the tiles run from the last
+// query tile (most key tiles) to the first, so the longest workgroups start
+// first and the short ones fill the tail.
 __device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bool causal,
                                           int &bh, int &qt) {
-  const int xcd = bid % kNumXcd;
-  const int slot = bid / kNumXcd;
-  const int base = nblocks / kNumXcd, extra = nblocks % kNumXcd;
-  const int logical = xcd * base + min(xcd, extra) + slot;
-  bh = logical / n_qtiles;
-  const int t = logical % n_qtiles;
+  const int n_heads = nblocks / n_qtiles;
+  int t;
+  if (n_heads % kNumXcd == 0) {
+    const int hpx = n_heads / kNumXcd;
+    const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+    t = slot / hpx;
+    bh = xcd * hpx + slot % hpx;
+  } else {
+    t = bid / n_heads;
+    bh = bid % n_heads;
+  }
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
@@ -107,6 +115,14 @@ __device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bo
 //    bytes and its partner group the next 32 bytes): slot c ^ swz_v(r) with
 //    swz_v(r) = 4 * (row index within the group of 4) so the 4 x 4 chunks of
 //    a group pair land in 16 distinct slots.
+//
+// Software pipeline (per wave, iteration j):
+//   phase 1: MFMAs of S(j+1) = K(j+1) Q^T   |  VALU: P(j) = exp2(S(j) c - m), to bf16
+//   phase 2: MFMAs of O += V(j)^T P(j)^T     |  VALU: mask and row max of S(j+1), sum of P(j)
+//   then, if some row's maximum grew past the slack, rescale O and l (rare).
+// K runs one tile ahead of V: iteration j reads K(j+1) and V(j); the loads
+// issued at its start fill K(j+2) and V(j+1), so every load has a whole
+// iteration to land before the barrier that publishes it.
 // ---------------------------------------------------------------------------
 template <int D, int BN, int NW>
 struct BfLayout {
@@ -124,36 +140,10 @@ struct BfLayout {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
 
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const lds_void *)p;
-}
-
-// ds_read_b64_tr_b16 issued as inline assembly. Through the builtin, the
-// compiler cannot tell these LDS reads from the asynchronous global->LDS loads
-// of the next tile (into the other stage) and waits for those loads to land
-// first; here it does not see an LDS access at all. The result must therefore
-// be released by lds_wait_all before use.
-__device__ __forceinline__ v2u32 ds_read_tr16_b64(uint32_t addr) {
-  v2u32 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-// Wait for all outstanding LDS reads; the registers passed through the asm tie
-// every later use of them to this wait.
-template <int N>
-__device__ __forceinline__ void lds_wait_all(v2u32 (&v)[N][2]) {
-  if constexpr (N == 2) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]));
-  } else {
-    static_assert(N == 4, "two or four 32-column blocks");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]),
-                   "+v"(v[2][0]), "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1]));
-  }
 }
 
 // Buffer resource over `bytes` bytes at `base` (raw, unswizzled; reads past the
@@ -163,13 +153,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 }
 
 // buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voffset into LDS
-// at `lds` + 16 * lane. The builtin exists only for the GPU target, and the
-// host compilation pass of a kernel template that names it drops the kernel's
-// launch stub, so it is compiled for the device pass alone (this function has
-// no host caller).
-__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voffset) {
+// at byte address `lds` (via M0) + 16 * lane. Written as inline assembly so
+// that the compiler does not treat every later LDS read as possibly aliasing
+// this asynchronous write (it would wait for the next tile's loads before
+// reading the current one); the kernel publishes the data itself with
+// s_waitcnt vmcnt(0) and a workgroup barrier. M0 is used by nothing else here.
+// The host compilation pass of the kernel templates never calls it.
+__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)lds, 16, voffset, 0, 0, 0);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
 #endif
 }
 
@@ -185,10 +180,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   using LY = BfLayout<D, BN, NW>;
   constexpr int BM = kRowsPerWave * NW;  // query rows per workgroup
   constexpr int NKB = BN / 32;           // 32-key MFMA blocks per tile
+  constexpr int NDB = D / 32;            // 32-column blocks of the output
+  constexpr int NCC = D / 16;            // 16-wide steps of the score contraction
   __shared__ __attribute__((aligned(1024))) char smem[2 * LY::STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: keep it in an SGPR
+  const int lane = tid % 64;
   const int l32 = lane % 32, hh = lane / 32;
 
   int bh, qt;
@@ -201,6 +199,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   const int q0 = qt * BM;
   const int qw = q0 + kRowsPerWave * wave;  // first query row of this wave
   const int qrow = qw + l32;                // the query row this lane carries
+  const bool wave_live = qw < N;            // wave has rows to compute (uniform)
 
   // Per-lane byte offsets (within a tile) of this wave's share of the tile loads:
   // LDS slot p = 1024 * gi + 16 * lane holds chunk (slot ^ swz(row)) of row p / ROW.
@@ -212,25 +211,25 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
     kvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_k(r));
     vvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_v(r));
   }
-  auto issue = [&](int t, int stage) {
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue_k = [&](int t) {
     const int k0 = t * BN;
-    const int bytes = (N - k0) * LY::ROW;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + (size_t)k0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vh + (size_t)k0 * D, bytes);
-    char *kdst = smem + stage * LY::STAGE;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Kh + (size_t)k0 * D, (N - k0) * LY::ROW);
+    const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + 1024 * wave * LY::LPW;
 #pragma unroll
-    for (int i = 0; i < LY::LPW; ++i) {
-      const int gi = wave * LY::LPW + i;
-      load_lds_16(kr, kdst + 1024 * gi, kvo[i]);
-      load_lds_16(vr, kdst + LY::TILE + 1024 * gi, vvo[i]);
-    }
+    for (int i = 0; i < LY::LPW; ++i) load_lds_16(rs, dst + 1024 * i, kvo[i]);
+  };
+  auto issue_v = [&](int t) {
+    const int k0 = t * BN;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Vh + (size_t)k0 * D, (N - k0) * LY::ROW);
+    const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + LY::TILE + 1024 * wave * LY::LPW;
+#pragma unroll
+    for (int i = 0; i < LY::LPW; ++i) load_lds_16(rs, dst + 1024 * i, vvo[i]);
   };
 
-  // K reads (A operand of S^T = K Q^T): row 32kb + l32, chunk 2cc + hh.
-  // The chunk index only flips bits 5..7 of the byte address, so a per-cc XOR
-  // of one base address gives every step.
-  const int krow = l32;
-  const int kbase = krow * LY::ROW + 16 * (hh ^ LY::swz_k(krow));
+  // K reads (A operand of S^T = K Q^T): row 32kb + l32, chunk 2cc + hh; the
+  // chunk index only flips bits 5..7 of the byte address.
+  const int kbase = l32 * LY::ROW + 16 * (hh ^ LY::swz_k(l32));
   // V transposing reads: 16-lane group g reads rows 4hh + (lane%16)/4 (+8u, +16mm,
   // +32kb) and columns 32db + 16(g%2) + 4(lane%4); in slot terms the column block
   // db is XORed with swz_v(row)/4.
@@ -239,147 +238,207 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   const int vbase = vrow * LY::ROW + 16 * (vchunk ^ LY::swz_v(vrow)) + 8 * (lane % 2);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16cc + 8hh + 0..7].
-  bf16x8 qf[D / 16];
+  bf16x8 qf[NCC];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) {
+  for (int cc = 0; cc < NCC; ++cc) {
     if (qrow < N)
       qf[cc] = *(const bf16x8 *)(Qh + (size_t)qrow * D + 16 * cc + 8 * hh);
     else
       qf[cc] = bf16x8{};
   }
 
-  f32x16 o[D / 32];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float m = -INFINITY;  // reference row maximum (base-2 scaled domain)
   float lsum = 0.f;     // row sum relative to m over this half-wave's keys
 
   const int kend = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kend + BN - 1) / BN;
+  const int nt = (kend + BN - 1) / BN;
   // Leading tiles that need no mask for any row of the workgroup.
   const int nfull = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
 
-  auto compute = [&](int t, int stage, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    const int k0 = t * BN;
-    if (EDGE && CAUSAL && k0 > qw + kRowsPerWave - 1) return;  // wholly after this wave's rows
-    const char *ks = smem + stage * LY::STAGE;
-    const char *vs = ks + LY::TILE;
+  // Is 32-key block kb of tile t needed by this wave? (always, off the edge)
+  auto block_live = [&](int t, int kb) {
+    const int kb0 = t * BN + 32 * kb;
+    return kb0 < N && (!CAUSAL || kb0 <= qw + kRowsPerWave - 1);
+  };
 
-    f32x16 s[NKB];
-    bool act[NKB];
+  // S^T blocks of 32 keys x 32 queries for tile t. Result layout: lane (l32, hh),
+  // register r holds key 8(r/4) + 4hh + r%4 of the block, query qrow.
+  auto scores = [&](int t, f32x16 (&s)[NKB], auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const char *ks = smem + (t & 1) * LY::STAGE;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int kb0 = k0 + 32 * kb;
-      act[kb] = !EDGE || ((kb0 < N) && (!CAUSAL || kb0 <= qw + kRowsPerWave - 1));
-      if (act[kb]) {
-#pragma unroll
-        for (int cc = 0; cc < D / 16; ++cc) {
-          const bf16x8 a = *(const bf16x8 *)(ks + 32 * kb * LY::ROW + (kbase ^ (32 * cc)));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc == 0 ? f32x16{} : s[kb], 0, 0, 0);
-        }
-        if (EDGE) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb0 + 8 * (r / 4) + 4 * hh + (r % 4);
-            const bool bad = key >= N || (CAUSAL && key > qrow);
-            s[kb][r] = bad ? -INFINITY : s[kb][r];
-          }
-        }
-      } else {
+      if (EDGE && !block_live(t, kb)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
+        continue;
+      }
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        const bf16x8 a = *(const bf16x8 *)(ks + 32 * kb * LY::ROW + (kbase ^ (32 * cc)));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc == 0 ? f32x16{} : s[kb], 0, 0, 0);
       }
     }
-
-    // Row maximum of the tile (16 keys per lane per block, then the partner half).
+  };
+  auto mask = [&](int t, f32x16 (&s)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int kb0 = t * BN + 32 * kb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb0 + 8 * (r / 4) + 4 * hh + (r % 4);
+        const bool bad = key >= N || (CAUSAL && key > qrow);
+        s[kb][r] = bad ? -INFINITY : s[kb][r];
+      }
+    }
+  };
+  auto rowmax = [&](const f32x16 (&s)[NKB]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = halves_max(mx);
+    return halves_max(mx);
+  };
+  // Move the reference maximum only when some row of the wave grew past the
+  // slack (always on the first tile, where m = -inf); rows that did not grow
+  // get alpha = 1.
+  auto update_ref = [&](float mx) {
     const float mc = mx * c;
-    // Move the reference maximum only when some row of the wave grew past the
-    // slack; rows that did not grow get alpha = 1.
     const bool grow = mc > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = grow ? mc : m;
       const float alpha = exp2_fast(m - m_new);  // 0 while m is still -inf
       lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = m_new;
     }
-    const float mref = (m == -INFINITY) ? 0.f : m;
-
-    float psum = 0.f;
+  };
+  // P = exp2(S c - m) in place, and its bf16 copy as the B operand (P^T) of the
+  // second MFMA: key half mm of block kb is registers 8mm..8mm+7 of s[kb].
+  auto exponentiate = [&](f32x16 (&s)[NKB], bf16x8 (&pb)[NKB][2]) {
+    const float mref = (m == -INFINITY) ? 0.f : m;  // no -inf - -inf
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kb][r], c, -mref));
-        s[kb][r] = p;
-        psum += p;
-      }
-    lsum += psum;
-
-    // O^T += V^T P^T. B operand (P^T) for key half mm of block kb is registers
-    // 8mm..8mm+7 of s[kb] (keys 16mm + 8(t/4) + 4hh + t%4 for slot t); the A
-    // operand (V^T) lists the same keys via two transposing reads of 4 keys.
+      for (int r = 0; r < 16; ++r) s[kb][r] = exp2_fast(fmaf(s[kb][r], c, -mref));
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) pb[kb][mm][t8] = (bf16)s[kb][8 * mm + t8];
+  };
+  auto rowsum = [&](const f32x16 (&s)[NKB]) {
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ps += s[kb][r];
+    return ps;
+  };
+  // O^T += V^T P^T for tile t. The A operand (V^T) lists the keys of P's slots
+  // 16mm + 8(t/4) + 4hh + t%4 via two transposing reads of 4 consecutive keys.
+  auto accumulate = [&](int t, const bf16x8 (&pb)[NKB][2], auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const char *vs = smem + (t & 1) * LY::STAGE + LY::TILE;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      if (!act[kb]) continue;
+      if (EDGE && !block_live(t, kb)) continue;
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        bf16x8 pb;
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) pb[t8] = (bf16)s[kb][8 * mm + t8];
         const int roff = (32 * kb + 16 * mm) * LY::ROW;
-        // All transposing reads of this key half first, then one LDS wait whose
-        // register operands order the MFMAs after it.
-        v2u32 vt[D / 32][2];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const uint32_t a0 = lds_addr(vs + roff + (vbase ^ (64 * db)));
-          vt[db][0] = ds_read_tr16_b64(a0);
-          vt[db][1] = ds_read_tr16_b64(a0 + 8 * LY::ROW);
-        }
-        lds_wait_all(vt);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int db = 0; db < NDB; ++db) {
+          const char *p0 = vs + roff + (vbase ^ (64 * db));
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0 + 8 * LY::ROW));
           const bf16x8 a = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(vt[db][0], vt[db][1], 0, 1, 2, 3));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][mm], o[db], 0, 0, 0);
         }
       }
     }
   };
-
-  // One barrier per tile: after it, every wave's share of tile t is in LDS and
-  // every wave has finished reading the other stage, which the loads of tile
-  // t+1 then overwrite while tile t is computed.
-  auto step = [&](int t, auto edge_tag) {
+  // All of this wave's loads issued so far have landed; after the barrier, so
+  // have every wave's, and every wave is done with the previous iteration.
+  auto publish = [&]() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
-    if (qw < N) compute(t, t & 1, edge_tag);
   };
-  issue(0, 0);
-  int t = 0;
-  for (; t < nfull; ++t) step(t, std::false_type{});
-  for (; t < ntiles; ++t) step(t, std::true_type{});
 
-  if (qw >= N) return;
+  // Iteration t: loads for K(t+2), V(t+1); S(t+1) next to P(t); O += V(t) P(t).
+  // The steady-state form (both tiles full, a next tile exists) is straight-line
+  // code; the generic form, used for the few tiles at the diagonal or the
+  // ragged end, tests its conditions at run time (all uniform).
+  auto iteration_full = [&](int t, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB]) {
+    publish();
+    if (t + 2 < nt) issue_k(t + 2);
+    issue_v(t + 1);
+    bf16x8 pb[NKB][2];
+    scores(t + 1, s_nxt, std::false_type{});
+    exponentiate(s_cur, pb);
+    accumulate(t, pb, std::false_type{});
+    lsum += rowsum(s_cur);
+    update_ref(rowmax(s_nxt));
+  };
+  auto iteration_edge = [&](int t, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB]) {
+    const bool has_next = t + 1 < nt;
+    publish();
+    if (t + 2 < nt) issue_k(t + 2);
+    if (has_next) issue_v(t + 1);
+    bf16x8 pb[NKB][2];
+    if (has_next) scores(t + 1, s_nxt, std::true_type{});
+    exponentiate(s_cur, pb);
+    accumulate(t, pb, std::true_type{});
+    lsum += rowsum(s_cur);
+    if (has_next) {
+      if (t + 1 >= nfull) mask(t + 1, s_nxt);
+      update_ref(rowmax(s_nxt));
+    }
+  };
+
+  f32x16 sa[NKB], sb[NKB];
+  // Prologue: K(0), V(0), K(1) in flight; S(0) and its reference maximum.
+  issue_k(0);
+  issue_v(0);
+  if (nt > 1) issue_k(1);
+  publish();
+  // Waves whose rows all lie past N (only in the last query tile of a ragged
+  // sequence) run the same code on zero Q rows and store nothing: no branch
+  // around the loop, so the Q loads are known complete before it.
+  // Tile 0 is computed for every block (the mask removes dead ones), so every
+  // path through here has consumed Q before the loop.
+  scores(0, sa, std::false_type{});
+  if (nfull == 0) mask(0, sa);
+  update_ref(rowmax(sa));
+
+  int t = 0;
+  // Steady state, two iterations per trip so that S(t) and S(t+1) swap
+  // registers without copies: both tiles after t are full tiles.
+  for (; t + 2 < nfull; t += 2) {
+    iteration_full(t, sa, sb);
+    iteration_full(t + 1, sb, sa);
+  }
+  for (; t < nt; t += 2) {
+    iteration_edge(t, sa, sb);
+    if (t + 1 < nt) iteration_edge(t + 1, sb, sa);
+  }
+
+  if (!wave_live) return;
   // Epilogue: one division by the row sum (both half-waves' keys), RNE to bf16.
   const float ltot = halves_sum(lsum);
   if (qrow < N) {
     const float inv = 1.f / ltot;
     bf16 *orow = O + head + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         bf16x4 v4;
