@@ -31,7 +31,8 @@ METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16, causal, B4 H16 N4096 d128)"
 # fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 KERNEL_SOURCE = os.path.join(ROOT, "tiled_online_softmax_amd", "csrc", "fa_fwd.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, per workload and kernel source.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_kernel_{}_traffic.json")
 
 
 def source_digest() -> str:
@@ -42,7 +43,7 @@ def source_digest() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed counter summary, if it matches this source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -67,9 +68,11 @@ def cpu_baseline(w, q, k, v, O, L, target_s: float):
         Oref, Lref = oracle.attention(qn, kn, vn, w.causal, w.scale, rows=rows)
         return rows, Oref, Lref, time.perf_counter() - t0
 
-    rows, Oref, Lref, t = run(8)
-    nrows = int(min(w.N, max(8, 8 * target_s / max(t, 1e-3))))
-    if nrows > 8:
+    nrows = 8
+    rows, Oref, Lref, t = run(nrows)
+    # Grow the sample until it takes at least half the target time (or covers every row).
+    while t < 0.5 * target_s and len(rows) < w.N:
+        nrows = int(min(w.N, max(2 * nrows, nrows * target_s / max(t, 1e-3))))
         rows, Oref, Lref, t = run(nrows)
     pairs = (rows + 1).sum() if w.causal else len(rows) * w.N
     flops = 4.0 * w.d * float(pairs) * heads
@@ -88,6 +91,24 @@ def cpu_baseline(w, q, k, v, O, L, target_s: float):
     }
 
 
+def copy_calibration(mib: int):
+    """Three device-to-device copies of a known size: each reads and writes `mib` MiB.
+
+    The sizes exceed the last-level cache, so every byte crosses HBM once each way;
+    the counters' readings for these dispatches give the factor between the
+    counter units and bytes.
+    """
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": n * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +118,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the causal bf16 B4 H16 N4096 d128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run three plain device copies of MIB MiB each "
+                         "(reference dispatches for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -105,6 +129,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import tiled_online_softmax_amd as fa
     from workloads import HEADLINE, WORKLOADS
