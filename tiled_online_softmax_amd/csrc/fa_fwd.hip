@@ -158,10 +158,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 // this asynchronous write (it would wait for the next tile's loads before
 // reading the current one); the kernel publishes the data itself with
 // s_waitcnt vmcnt(0) and a workgroup barrier. M0 is used by nothing else here.
+// On GFX9-family GPUs an LDS DMA must not read M0 in the instruction right
+// after the SALU write of M0: without the wait state (s_nop 0) the load can
+// still see the previous M0 and land in the previous chunk's slot.
 // The host compilation pass of the kernel templates never calls it.
 __device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
