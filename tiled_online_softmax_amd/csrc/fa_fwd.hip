@@ -152,22 +152,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-// buffer_load_dwordx4 ... lds: 16 bytes per lane from rsrc + voffset into LDS
-// at byte address `lds` (via M0) + 16 * lane. Written as inline assembly so
-// that the compiler does not treat every later LDS read as possibly aliasing
-// this asynchronous write (it would wait for the next tile's loads before
-// reading the current one); the kernel publishes the data itself with
-// s_waitcnt vmcnt(0) and a workgroup barrier. M0 is used by nothing else here.
+// One wave's share of a tile matrix, LPW x buffer_load_dwordx4 ... lds: load i
+// moves 16 bytes per lane from rsrc + vo[i] + 1024 i into LDS at byte address
+// `lds` (via M0) + 1024 i + 16 * lane. The instruction offset (1024 i) is added
+// to both the buffer offset, inside the range check, and the LDS address, so
+// M0 is written once per share. Written as inline assembly so that the
+// compiler does not treat every later LDS read as possibly aliasing these
+// asynchronous writes (it would wait for the next tile's loads before reading
+// the current one); the kernel publishes the data itself with s_waitcnt
+// vmcnt(0) and a workgroup barrier. M0 is used by nothing else here.
 // On GFX9-family GPUs an LDS DMA must not read M0 in the instruction right
 // after the SALU write of M0: without the wait state (s_nop 0) the load can
-// still see the previous M0 and land in the previous chunk's slot.
+// still see the previous M0 and land in the previous share's slots.
 // The host compilation pass of the kernel templates never calls it.
-__device__ __forceinline__ void load_lds_16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset) {
+template <int LPW>
+__device__ __forceinline__ void load_lds_share(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, const int (&vo)[LPW]) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
+  static_assert(LPW == 2 || LPW == 4, "one wave issues 2 or 4 loads per tile matrix");
+  if constexpr (LPW == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds"
+                 :
+                 : "s"(lds), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(rsrc)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+                 :
+                 : "s"(lds), "v"(vo[0]), "v"(vo[1]), "s"(rsrc)
+                 : "memory", "m0");
 #endif
 }
 
@@ -206,28 +223,27 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
 
   // Per-lane byte offsets (within a tile) of this wave's share of the tile loads:
   // LDS slot p = 1024 * gi + 16 * lane holds chunk (slot ^ swz(row)) of row p / ROW.
+  // Load i adds 1024 i through its instruction offset, so it is taken out here.
   int kvo[LY::LPW], vvo[LY::LPW];
 #pragma unroll
   for (int i = 0; i < LY::LPW; ++i) {
     const int p = 64 * (wave * LY::LPW + i) + lane;  // 16-byte slot index in the tile
     const int r = p / LY::CPR, j = p % LY::CPR;
-    kvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_k(r));
-    vvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_v(r));
+    kvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_k(r)) - 1024 * i;
+    vvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_v(r)) - 1024 * i;
   }
   const uint32_t smem_lds = lds_addr(smem);
   auto issue_k = [&](int t) {
     const int k0 = t * BN;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(Kh + (size_t)k0 * D, (N - k0) * LY::ROW);
     const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + 1024 * wave * LY::LPW;
-#pragma unroll
-    for (int i = 0; i < LY::LPW; ++i) load_lds_16(rs, dst + 1024 * i, kvo[i]);
+    load_lds_share(rs, dst, kvo);
   };
   auto issue_v = [&](int t) {
     const int k0 = t * BN;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(Vh + (size_t)k0 * D, (N - k0) * LY::ROW);
     const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + LY::TILE + 1024 * wave * LY::LPW;
-#pragma unroll
-    for (int i = 0; i < LY::LPW; ++i) load_lds_16(rs, dst + 1024 * i, vvo[i]);
+    load_lds_share(rs, dst, vvo);
   };
 
   // K reads (A operand of S^T = K Q^T): row 32kb + l32, chunk 2cc + hh; the
