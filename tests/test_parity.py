@@ -98,6 +98,16 @@ def test_workload_full_size_sampled(fa, name):
     assert bool((L <= row_bound + logn + 1e-2).all()), "L above its Cauchy-Schwarz bound"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_f32_long_sampled(fa, causal, d):
+    """fp32 at N = 4100: 129 key tiles spread over the waves of a workgroup (uneven
+    shares, a ragged last tile), checked on sampled rows."""
+    q, k, v = make_qkv(2, 4, 4100, d, "f32", seed=51 + d)
+    rows = sample_rows(4100, 24, seed=52)
+    _check(fa, q, k, v, causal, default_scale(d), "f32", rows=rows, label=f"fp32 N=4100 d={d} causal={causal}")
+
+
 EDGE_N = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 1000]
 
 
@@ -154,14 +164,16 @@ def test_uniform_closed_form(fa, dtype):
     assert float((L.double().cpu() - torch.log(torch.arange(1, N + 1, dtype=torch.float64))).abs().max()) <= ltol
 
 
-@pytest.mark.parametrize("B,H,N,d,causal", [(2, 4, 777, 128, True), (1, 2, 255, 128, True),
-                                             (1, 8, 1000, 64, False), (4, 16, 4096, 128, True)])
-def test_deterministic(fa, B, H, N, d, causal):
-    """Each output element is reduced in a fixed order, so repeated launches on the same
-    inputs are bitwise identical. A K/V tile landing in the wrong LDS slot (a DMA issued
-    before its LDS address took effect) or read before it landed shows up here as
-    launch-to-launch differences."""
-    q, k, v = make_qkv(B, H, N, d, "bf16", seed=48)
+@pytest.mark.parametrize("B,H,N,d,causal,dtype", [(2, 4, 777, 128, True, "bf16"), (1, 2, 255, 128, True, "bf16"),
+                                                   (1, 8, 1000, 64, False, "bf16"), (4, 16, 4096, 128, True, "bf16"),
+                                                   (8, 1, 1024, 64, False, "f32"), (2, 3, 777, 128, True, "f32")])
+def test_deterministic(fa, B, H, N, d, causal, dtype):
+    """Each output element is reduced in a fixed order (the fp32 kernel merges its waves'
+    partial results in wave order), so repeated launches on the same inputs are bitwise
+    identical. A K/V tile landing in the wrong LDS slot (a DMA issued before its LDS
+    address took effect) or read before it landed shows up here as launch-to-launch
+    differences."""
+    q, k, v = make_qkv(B, H, N, d, dtype, seed=48)
     dev = torch.device("cuda:0")
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     O1, L1 = fa.forward(qd, kd, vd, causal=causal, scale=default_scale(d))

@@ -14,8 +14,10 @@
 // softmax fragment of "Case Study: metal-flash-attention".
 //
 // gfx950 mapping (see the layout comments at each step):
-//  * A workgroup of four wave64s owns 128 query rows; each wave owns 32 rows
-//    and keeps its Q rows in VGPRs for the whole key loop.
+//  * bf16: a workgroup of four wave64s owns 128 query rows; each wave owns 32
+//    rows and keeps its Q rows in VGPRs for the whole key loop. fp32: a
+//    workgroup owns 32 query rows and its waves split the key tiles, merging
+//    their partial (m, l, O) through LDS at the end.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //    (bf16) or v_mfma_f32_32x32x2_f32 (fp32). In the result layout a lane holds
 //    16 keys of ONE query, so the row maximum and row sum are 16 in-lane ops
@@ -24,8 +26,10 @@
 //  * The same registers, converted to bf16, are the B operand of the second
 //    contraction O^T += V^T P^T with no data movement; V^T comes straight out
 //    of LDS with ds_read_b64_tr_b16 (transposing 4-key x 16-column blocks).
-//  * K/V tiles of 64 keys are staged through padded LDS rows; the global loads
-//    of tile j+1 are in flight while tile j is computed.
+//  * bf16: K/V tiles of 64 keys are copied global -> LDS (XOR-swizzled rows)
+//    two tiles ahead of their use. fp32: each wave loads its 32-key K/V
+//    operands straight into VGPRs, the next tile's loads in flight while the
+//    current tile is computed.
 //  * Scores are scaled into the base-2 domain (scale * log2 e folded into one
 //    FMA) and exponentiated with v_exp_f32.
 //  * Causal: key tiles wholly after the query tile are never loaded, 32-key
@@ -54,9 +58,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;     // four wave64s
 constexpr int kRowsPerWave = 32;  // query rows per wave (MFMA N dimension)
-constexpr int kBlockM = 128;      // query rows per workgroup
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -235,13 +237,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   const uint32_t smem_lds = lds_addr(smem);
   auto issue_k = [&](int t) {
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Kh + (size_t)k0 * D, (N - k0) * LY::ROW);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Kh + (size_t)k0 * D, min(N - k0, BN) * LY::ROW);
     const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + 1024 * wave * LY::LPW;
     load_lds_share(rs, dst, kvo);
   };
   auto issue_v = [&](int t) {
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Vh + (size_t)k0 * D, (N - k0) * LY::ROW);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Vh + (size_t)k0 * D, min(N - k0, BN) * LY::ROW);
     const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + LY::TILE + 1024 * wave * LY::LPW;
     load_lds_share(rs, dst, vvo);
   };
@@ -471,161 +473,216 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: everything in fp32 (v_mfma_f32_32x32x2_f32); P is not rounded.
-// Same work mapping and state layout as the bf16 kernel. The contraction over
-// d is split between the half-waves as d = hh * D/2 + cc, so each lane reads
-// contiguous runs of K and Q.
+//
+// Work mapping: one workgroup per (head, block of 32 query rows). Its NW waves
+// all carry the same 32 rows and split the block's 32-key tiles round-robin
+// (wave w takes tiles w, w + NW, ...), each with its own running m, l and
+// accumulator; the NW partial states are merged through LDS at the end with
+// the same rescaling rule that merges two key blocks (the recurrence is
+// associative over key blocks). This fills the GPU with 32-row blocks where a
+// 128-row tile would leave most CUs idle (8 heads x 1024 rows is 256
+// workgroups here, 64 with 128-row tiles), and no LDS or barrier is needed in
+// the key loop: every wave reads its K and V operands straight from global
+// memory (L2) into VGPRs with range-checked buffer loads, the next tile's
+// loads in flight while the current tile is computed.
+//
+// Operand layouts (lane = 32 hh + l32):
+//  * S^T = K Q^T, step s (< D/2): A = K[key l32][hh D/2 + s], B = Q[row l32][hh
+//    D/2 + s], so each lane reads D/2 contiguous floats of one K row and keeps
+//    D/2 floats of its Q row.
+//  * O^T += V^T P^T: the 32x32 output blocks db < D/32 hold columns NDB i + db
+//    (row i of the block), so at step r the A operands of all blocks are the
+//    NDB consecutive floats V[key][NDB l32 ..], one vector load, and the B
+//    operand is register r of the scores (key 8(r/4) + 4hh + r%4), as in the
+//    bf16 kernel. In the result a lane holds 4 NDB consecutive output columns
+//    per group r/4.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_f32_kernel(
-    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
-    float *__restrict__ O, float *__restrict__ L, int N, int n_qtiles, float c) {
-  constexpr int BN = 32;      // keys per LDS tile
-  constexpr int KS = D + 8;   // row strides in LDS (floats)
-  constexpr int VS = D + 8;
-  constexpr int CPR = D / 4;  // 16-byte chunks per row
-  constexpr int PER_T = BN * CPR / kThreads;
-  constexpr int HD = D / 2;
-  static_assert(BN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
+template <int N_>
+struct F32Vec;
+template <>
+struct F32Vec<2> {
+  typedef float type __attribute__((ext_vector_type(2)));
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(type, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+};
+template <>
+struct F32Vec<4> {
+  typedef f32x4 type;
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(type, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+};
 
-  __shared__ __attribute__((aligned(16))) float Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) float Vs[BN * VS];
+constexpr int kF32Rows = 32;  // query rows per workgroup (fp32 kernel)
+constexpr int kF32Keys = 32;  // keys per tile (fp32 kernel)
+
+// Two workgroups of four waves per CU at d = 64 (at most 256 VGPRs a wave, so
+// the MFMA accumulators stay in VGPRs and are rescaled in place).
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 2 : 1) void fa_fwd_f32_kernel(
+    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
+    float *__restrict__ O, float *__restrict__ L, int N, int n_qblocks, float c) {
+  constexpr int BN = kF32Keys;
+  constexpr int HD = D / 2;    // contraction steps of S^T per tile
+  constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  constexpr int ROW = D * 4;   // bytes per row
+  constexpr int OS = D + 4;    // row stride (floats) of the merge buffer
+  using VV = F32Vec<NDB>;
+  typedef typename VV::type vvec;
+
+  __shared__ __attribute__((aligned(16))) float Os[NW][kF32Rows * OS];
+  __shared__ float Ms[NW][kF32Rows], Ls[NW][kF32Rows];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
-  const int l32 = lane % 32, hh = lane / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, l32 = lane % 32, hh = lane / 32;
 
-  int bh, qt;
-  map_block(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, bh, qt);
+  int bh, qb;
+  map_block(blockIdx.x, gridDim.x, n_qblocks, CAUSAL, bh, qb);
   const size_t head = (size_t)bh * (size_t)N * D;
-  const float *Qh = Q + head;
   const float *Kh = K + head;
   const float *Vh = V + head;
+  const int q0 = qb * kF32Rows;
+  const int qrow = q0 + l32;
 
-  const int q0 = qt * kBlockM;
-  const int qw = q0 + kRowsPerWave * wave;
-  const int qrow = qw + l32;
-
-  // B operand of S^T = K Q^T for step cc: Q[qrow][hh * D/2 + cc].
+  // Q rows of the block (rows past N read as zero).
   float qf[HD];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head + (size_t)q0 * D, min(N - q0, kF32Rows) * ROW);
 #pragma unroll
-  for (int c4 = 0; c4 < HD / 4; ++c4) {
-    f32x4 v = (qrow < N) ? *(const f32x4 *)(Qh + (size_t)qrow * D + hh * HD + 4 * c4) : f32x4{};
+    for (int j = 0; j < HD / 4; ++j) {
+      const f32x4 w = F32Vec<4>::load(rq, l32 * ROW + hh * HD * 4 + 16 * j);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) qf[4 * c4 + e] = v[e];
+      for (int e = 0; e < 4; ++e) qf[4 * j + e] = w[e];
+    }
   }
 
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  float m = -INFINITY, lsum = 0.f;
+  const int kend = CAUSAL ? min(N, q0 + kF32Rows) : N;
+  const int nt = (kend + BN - 1) / BN;
 
-  const int kend = CAUSAL ? min(N, q0 + kBlockM) : N;
-  const int ntiles = (kend + BN - 1) / BN;
-
-  u32x4 kr[PER_T], vr[PER_T];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      const int key = t * BN + row;
-      if (key < N) {
-        kr[i] = *(const u32x4 *)(Kh + (size_t)key * D + 4 * ch);
-        vr[i] = *(const u32x4 *)(Vh + (size_t)key * D + 4 * ch);
-      } else {
-        kr[i] = u32x4{};
-        vr[i] = u32x4{};
-      }
-    }
-  };
-  auto swrite = [&]() {
-#pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      *(u32x4 *)(&Ks[row * KS + 4 * ch]) = kr[i];
-      *(u32x4 *)(&Vs[row * VS + 4 * ch]) = vr[i];
-    }
-  };
-
-  gload(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    swrite();
-    __syncthreads();
-    if (t + 1 < ntiles) gload(t + 1);
-
-    if (qw >= N) continue;
+  f32x4 kf[HD / 4];  // K operand of one tile
+  vvec vf[16];       // V operands of one tile, one vector per MFMA step
+  auto load_k = [&](int t) {
     const int k0 = t * BN;
-    if (CAUSAL && k0 > qw + kRowsPerWave - 1) continue;  // block wholly after this wave's rows
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)k0 * D, min(N - k0, BN) * ROW);
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) kf[j] = F32Vec<4>::load(rk, l32 * ROW + hh * HD * 4 + 16 * j);
+  };
+  auto load_v = [&](int t) {
+    const int k0 = t * BN;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)k0 * D, min(N - k0, BN) * ROW);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      vf[r] = VV::load(rv, (8 * (r / 4) + 4 * hh + r % 4) * ROW + NDB * 4 * l32);
+  };
 
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;  // m: reference row maximum in the base-2 domain
+
+  if (wave < nt) {
+    load_k(wave);
+    load_v(wave);
+  }
+  for (int t = wave; t < nt; t += NW) {
+    const int k0 = t * BN;
+    const bool more = t + NW < nt;
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int c4 = 0; c4 < HD / 4; ++c4) {
-      const f32x4 a4 = *(const f32x4 *)(&Ks[l32 * KS + hh * HD + 4 * c4]);
+    for (int j = 0; j < HD / 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[e], qf[4 * c4 + e], s, 0, 0, 0);
-    }
-    const bool edge = (k0 + 31 >= N) || (CAUSAL && k0 + 31 > qw);
-    if (edge) {
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[j][e], qf[4 * j + e], s, 0, 0, 0);
+    if (more) load_k(t + NW);
+
+    // Ragged end and the causal diagonal tile (k0 == q0) only.
+    if (k0 + BN > N || (CAUSAL && k0 + BN > q0)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 8 * (r / 4) + 4 * hh + (r % 4);
+        const int key = k0 + 8 * (r / 4) + 4 * hh + r % 4;
         if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
       }
     }
-
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = halves_max(mx);
-    const float m_new = fmaxf(m, mx * c);
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m - m_ref);
-    m = m_new;
-
-    float psum = 0.f;
+    mx = halves_max(mx) * c;
+    // The reference m moves (and O, l are rescaled) only when some row of the
+    // wave exceeds it by more than the slack.
+    const bool grow = mx > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = exp2_fast(m - m_new);  // 0 while m is still -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = m_new;
+    }
+    const float m_ref = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = exp2_fast(fmaf(s[r], c, -m_ref));
-      s[r] = p;
-      psum += p;
+      s[r] = exp2_fast(fmaf(s[r], c, -m_ref));
+      lsum += s[r];
     }
-    lsum = fmaf(alpha, lsum, psum);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-    // O^T += V^T P^T, two keys per MFMA: key slot hh of step r is key
-    // 8(r/4) + 4hh + r%4, whose P value is register r of this lane.
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int vrow = 8 * (r / 4) + 4 * hh + (r % 4);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const float a = Vs[vrow * VS + 32 * db + l32];
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[r], o[db], 0, 0, 0);
-      }
-    }
+      for (int db = 0; db < NDB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[r][db], s[r], o[db], 0, 0, 0);
+    if (more) load_v(t + NW);
   }
 
-  if (qw >= N) return;
-  const float ltot = halves_sum(lsum);
-  if (qrow < N) {
-    const float inv = 1.f / ltot;
-    float *orow = O + head + (size_t)qrow * D;
+  // Merge the NW partial states of each row: M = max_w m_w, weights 2^(m_w - M).
+  const float lw = halves_sum(lsum);
+  if (hh == 0) {
+    Ms[wave][l32] = m;
+    Ls[wave][l32] = lw;
+  }
+  __syncthreads();
+  float mtot = -INFINITY;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int w = 0; w < NW; ++w) mtot = fmaxf(mtot, Ms[w][l32]);
+  const float f = exp2_fast(m - mtot);  // 0 for a wave that saw no key tile
+  {
+    float *orow = &Os[wave][l32 * OS];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v4;
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = o[db][4 * g + e] * inv;
-        *(f32x4 *)(orow + 32 * db + 8 * g + 4 * hh) = v4;
+      for (int h = 0; h < NDB; ++h) {
+        // floats 4h .. 4h+3 of the 4 NDB consecutive columns of group g
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * h + e;  // (r % 4) * NDB + db
+          v[e] = o[idx % NDB][4 * g + idx / NDB] * f;
+        }
+        *(f32x4 *)(orow + NDB * (8 * g + 4 * hh) + 4 * h) = v;
       }
-    if (hh == 0) L[(size_t)bh * N + qrow] = (m + log2_fast(ltot)) * kLn2;
+  }
+  __syncthreads();
+  // Sum the partial outputs, divide once by the merged row sum, store.
+  constexpr int C4 = D / 4;
+  static_assert(kF32Rows * C4 % (NW * 64) == 0, "merge must split evenly over the workgroup");
+#pragma unroll
+  for (int it = 0; it < kF32Rows * C4 / (NW * 64); ++it) {
+    const int idx = tid + NW * 64 * it;
+    const int row = idx / C4, c4 = idx % C4;
+    if (q0 + row >= N) continue;
+    float mrow = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mrow = fmaxf(mrow, Ms[w][row]);
+    float lrow = 0.f;
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      lrow = fmaf(Ls[w][row], exp2_fast(Ms[w][row] - mrow), lrow);
+      acc += *(const f32x4 *)(&Os[w][row * OS + 4 * c4]);
+    }
+    const float inv = 1.f / lrow;
+    *(f32x4 *)(O + head + (size_t)(q0 + row) * D + 4 * c4) = acc * inv;
+    if (c4 == 0) L[(size_t)bh * N + q0 + row] = (mrow + log2_fast(lrow)) * kLn2;
   }
 }
 
@@ -657,12 +714,18 @@ hipError_t launch_bf16(int64_t BH, int N, hipStream_t s, const void *Q, const vo
                 64 * kBf16Waves, s, Q, K, V, O, L, N, nq, c);
 }
 
+// Waves per workgroup of the fp32 kernel (each takes every NW-th key tile).
+#ifndef FA_F32_NW
+#define FA_F32_NW 4
+#endif
+constexpr int kF32Waves = FA_F32_NW;
+
 template <int D, bool CAUSAL>
 hipError_t launch_f32(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
                       const void *V, void *O, float *L, float c) {
-  const int nq = (N + kBlockM - 1) / kBlockM;
-  const void *kern = (const void *)&fa_fwd_f32_kernel<D, CAUSAL>;
-  return launch(kern, (int)(BH * nq), kThreads, s, Q, K, V, O, L, N, nq, c);
+  const int nq = (N + kF32Rows - 1) / kF32Rows;
+  const void *kern = (const void *)&fa_fwd_f32_kernel<D, CAUSAL, kF32Waves>;
+  return launch(kern, (int)(BH * nq), 64 * kF32Waves, s, Q, K, V, O, L, N, nq, c);
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -683,7 +746,8 @@ extern "C" fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void 
   // Sizes: 32-bit row indices inside a head, grid size below 2^31.
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (N > (int64_t)1 << 24) return FA_ERR_UNSUPPORTED;
-  const int64_t n_qtiles = (N + kBlockM - 1) / kBlockM;
+  const int64_t block_rows = dtype == FA_DTYPE_BF16 ? kRowsPerWave * kBf16Waves : kF32Rows;
+  const int64_t n_qtiles = (N + block_rows - 1) / block_rows;
   if (B * H > ((int64_t)1 << 31) / n_qtiles - 1) return FA_ERR_UNSUPPORTED;
   const size_t nelem = (size_t)B * (size_t)H * (size_t)N * (size_t)d;
   const size_t obytes = nelem * esize, lbytes = (size_t)B * H * N * sizeof(float);
