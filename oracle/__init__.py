@@ -5,20 +5,25 @@ benchmark's CPU-baseline leg may import this package. The product path (the HIP
 library and its Python binding) never imports, links or calls anything here,
 and nothing here imports the product path.
 
-Two parts:
+Three parts:
 
 * ``attention`` -- standard attention by its definition (``attention.c``):
   "Writing a FlashAttention kernel in Metal", section "Standard attention", with
   the causal rule of its section "Blockwise attention and causal masking", and L
   as defined in "FlashAttention-2 from PyTorch to Triton", section "What We Are
   Building".
+* ``attention_bwd`` -- the gradients of that function with respect to Q, K and V
+  for a given output gradient, by the chain rule through its definition
+  (``attention_bwd.c``).
 * ``blockwise`` -- fp64 models of the pages' online-softmax recurrences (the
   method itself), used by the tests to tie the recurrence to the definition.
 
-Pins: every function here is checked, in ``tests/test_oracle.py`` and
-``tests/test_blockwise.py``, against closed forms, invariants, brute force on
-tiny inputs, torch's own scaled-dot-product attention in fp64 and the worked
-two-block example of the first page's "Online softmax" section.
+Pins: every function here is checked, in ``tests/test_oracle.py``,
+``tests/test_oracle_bwd.py`` and ``tests/test_blockwise.py``, against closed
+forms, invariants, brute force on tiny inputs (central differences of the
+forward oracle for the gradients), torch's own scaled-dot-product attention in
+fp64 (and its autograd) and the worked two-block example of the first page's
+"Online softmax" section.
 """
 
 from __future__ import annotations
@@ -31,14 +36,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attention.c")
+_SRC_BWD = os.path.join(_HERE, "attention_bwd.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
 def build(verbose: bool = False) -> str:
-    """Compile ``attention.c`` into ``liboracle.so`` with gcc (no fast-math)."""
+    """Compile ``attention.c`` and ``attention_bwd.c`` into ``liboracle.so`` with gcc (no fast-math)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-o", _LIB_PATH, _SRC, "-lm"]
+           "-o", _LIB_PATH, _SRC, _SRC_BWD, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -46,7 +52,8 @@ def build(verbose: bool = False) -> str:
 
 
 def load_library(path: str):
-    """Open a compiled copy of ``attention.c`` and declare its signatures."""
+    """Open a compiled copy of the oracle sources and declare its signatures (a copy
+    built from ``attention.c`` alone has no backward entry)."""
     lib = ctypes.CDLL(path)
     lib.oracle_attention_f64.restype = ctypes.c_int
     lib.oracle_attention_f64.argtypes = [
@@ -56,13 +63,20 @@ def load_library(path: str):
     ]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    if hasattr(lib, "oracle_attention_bwd_f64"):
+        lib.oracle_attention_bwd_f64.restype = ctypes.c_int
+        lib.oracle_attention_bwd_f64.argtypes = [ctypes.c_void_p] * 7 + [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_double,
+        ]
     return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+                os.path.getmtime(_SRC), os.path.getmtime(_SRC_BWD)):
             build()
         _lib = load_library(_LIB_PATH)
     return _lib
@@ -112,3 +126,35 @@ def attention(Q, K, V, causal: bool, scale: float, rows=None, lib=None):
     if squeeze:
         return O[0, 0], L[0, 0]
     return O, L
+
+
+def attention_bwd(Q, K, V, dO, causal: bool, scale: float, lib=None):
+    """Gradients of standard attention in fp64.
+
+    Q, K, V, dO: array-likes of shape [B, H, N, d] (or [N, d], treated as B=H=1),
+    up-cast losslessly to fp64; dO is the gradient of the loss with respect to the
+    output O = softmax(scale Q K^T) V (causal as in ``attention``).
+
+    Returns (dQ, dK, dV) as fp64 numpy arrays of the input shape.
+    ``lib`` selects another compiled copy (from ``load_library``); default: this one.
+    """
+    lib = lib or _load()
+    arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.float64)) for x in (Q, K, V, dO)]
+    squeeze = arrs[0].ndim == 2
+    if squeeze:
+        arrs = [a[None, None] for a in arrs]
+    q, k, v, go = arrs
+    if q.ndim != 4 or any(a.shape != q.shape for a in arrs):
+        raise ValueError(f"expected equal [B,H,N,d] shapes, got {[a.shape for a in arrs]}")
+    B, H, N, d = q.shape
+    dQ = np.empty_like(q)
+    dK = np.empty_like(q)
+    dV = np.empty_like(q)
+    st = lib.oracle_attention_bwd_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, go.ctypes.data,
+                                      dQ.ctypes.data, dK.ctypes.data, dV.ctypes.data,
+                                      B, H, N, d, 1 if causal else 0, float(scale))
+    if st != 0:
+        raise RuntimeError(f"oracle_attention_bwd_f64 failed with status {st}")
+    if squeeze:
+        return dQ[0, 0], dK[0, 0], dV[0, 0]
+    return dQ, dK, dV
