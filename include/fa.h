@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the tiled online-softmax attention forward pass (gfx950).
+ * fa.h -- C ABI of the tiled online-softmax attention forward and backward
+ * passes (gfx950).
  *
  * The operation is exact scaled-dot-product attention with the per-row
  * logsumexp, as defined in "Writing a FlashAttention kernel in Metal"
@@ -66,6 +67,40 @@ typedef enum {
  * concurrently; they share no state.
  */
 fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void *O, float *L,
+                   int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                   void *stream, int dtype);
+
+/*
+ * fa_bwd -- attention backward pass over B*H independent heads: the gradients
+ * of a loss with respect to Q, K and V, given its gradient dO with respect to
+ * O, for the same function fa_fwd computes. L is treated as an auxiliary
+ * output of the forward pass (not differentiated). The probabilities are
+ * recomputed from L as P = exp(S - L) ("FlashAttention-2 from PyTorch to
+ * Triton", section "What We Are Building"), so nothing N x N is stored, and
+ * the work is split into a dQ kernel and a dK/dV kernel that each own their
+ * outputs (as "Case Study: metal-flash-attention" describes for that
+ * project's backward pass).
+ *
+ *   Q, K, V  the forward inputs: device, contiguous [B][H][N][d] of `dtype`.
+ *   O, L     the forward outputs of fa_fwd for these inputs (same layouts).
+ *   dO       device, contiguous [B][H][N][d] of `dtype`: gradient w.r.t. O.
+ *   dQ,dK,dV device, contiguous [B][H][N][d] of `dtype`; written, rounded to
+ *            nearest even when bf16. They must not overlap each other, the
+ *            inputs or `work`.
+ *   work     device workspace of 2*B*H*N floats, overwritten (per row: the
+ *            sum over c of dO*O, then L * log2 e). Owned by the caller; its
+ *            contents after the call carry no meaning.
+ *   B,H,N,d, causal, scale, stream: as for fa_fwd.
+ *   dtype    FA_DTYPE_BF16 (FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED).
+ *
+ * dS = P o (dP - D) with dP = dO V^T and D_i = sum_c dO[i][c] O[i][c];
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO; accumulation in fp32, P and
+ * dS rounded to bf16 as MFMA operands. Ownership, asynchrony and validation as
+ * for fa_fwd: the library allocates no memory; on an error nothing is
+ * enqueued and the outputs are untouched.
+ */
+fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const void *O, const float *L,
+                   const void *dO, void *dQ, void *dK, void *dV, float *work,
                    int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                    void *stream, int dtype);
 

@@ -22,7 +22,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_fwd", "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -86,3 +86,40 @@ def test_misaligned(kw):
 
 def test_validation_order_null_before_unsupported():
     assert call(Q=0, d=96) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+# fa_bwd: ten 1 MiB-spaced fake buffers (tensors of 1*1*64*64 bf16 are 8 KiB).
+BWD = dict(Q=A, K=2 * A, V=3 * A, O=4 * A, L=5 * A, dO=6 * A, dQ=7 * A, dK=8 * A, dV=9 * A, work=10 * A)
+
+
+def call_bwd(B=1, H=1, N=64, d=64, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16, **kw):
+    p = dict(BWD, **kw)
+    return fa.raw_fa_bwd(p["Q"], p["K"], p["V"], p["O"], p["L"], p["dO"], p["dQ"], p["dK"], p["dV"],
+                         p["work"], B, H, N, d, causal, scale, None, dtype)
+
+
+@pytest.mark.parametrize("name", sorted(BWD))
+def test_bwd_null_pointer(name):
+    assert call_bwd(**{name: 0}) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(scale=0.0), dict(scale=float("nan")),
+                                dict(dtype=7)])
+def test_bwd_bad_arguments(kw):
+    assert call_bwd(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(dtype=fa.FA_DTYPE_F32), dict(N=(1 << 24) + 1)])
+def test_bwd_unsupported(kw):
+    assert call_bwd(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(dQ=2 * A + 64), dict(dK=6 * A), dict(dV=7 * A + 4096),
+                                dict(work=A + 32), dict(work=8 * A + 16), dict(dQ=5 * A)])
+def test_bwd_overlapping_outputs(kw):
+    assert call_bwd(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("name", ["Q", "dO", "dK", "work", "L"])
+def test_bwd_misaligned(name):
+    assert call_bwd(**{name: BWD[name] + 4}) == fa.FA_ERR_MISALIGNED

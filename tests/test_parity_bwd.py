@@ -1,0 +1,113 @@
+"""GPU parity of the backward pass (fa_bwd through the C ABI) against the fp64 oracle.
+
+Tolerance (bf16): max |dX_gpu - dX_ref| <= 1e-2 * max(1, max |dX_ref|) for each of dQ,
+dK, dV. The outputs are rounded to bf16 (relative error <= 2^-9), and each product
+term of the gradient carries one more bf16 rounding of P or dS as an MFMA operand
+(<= 2^-9 relative). The forward's O, rounded to bf16, enters D = sum_c dO O. A budget
+of five units of 2^-9 (~1e-2) of the largest entry covers these; the measured errors
+are 2.5e-3 to 5e-3 of it.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import default_scale, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import tiled_online_softmax_amd
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return tiled_online_softmax_amd
+
+
+def _inputs(B, H, N, d, seed, sigma_qk=1.0):
+    q, k, v = make_qkv(B, H, N, d, "bf16", seed=seed, sigma_qk=sigma_qk)
+    g = torch.Generator().manual_seed(seed + 1)
+    do = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    return q, k, v, do
+
+
+def _run(fa, q, k, v, do, causal, scale):
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    O, L = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.backward(qd, kd, vd, O, L, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _check(fa, q, k, v, do, causal, scale, label):
+    got = _run(fa, q, k, v, do, causal, scale)
+    ref = oracle.attention_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                               do.double().numpy(), causal, scale)
+    for name, a, r in zip(("dQ", "dK", "dV"), got, ref):
+        a = a.double().cpu().numpy()
+        assert np.isfinite(a).all(), f"{label}: {name} not finite"
+        err = float(np.abs(a - r).max())
+        bound = TOL * max(1.0, float(np.abs(r).max()))
+        print(f"[parity-bwd] {label} {name} max|err|={err:.3e} (tol {bound:.3e})", flush=True)
+        assert err <= bound, f"{label}: {name} error {err} > {bound}"
+
+
+EDGE_N = [1, 2, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 255, 257]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", EDGE_N)
+def test_bwd_edge_sizes(fa, N, causal, d):
+    q, k, v, do = _inputs(1, 2, N, d, seed=2000 + N + d)
+    _check(fa, q, k, v, do, causal, default_scale(d), f"N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 4, 512, 128, True), (1, 3, 1000, 64, False),
+                                             (1, 8, 640, 128, False), (1, 8, 640, 64, True)])
+def test_bwd_heads(fa, B, H, N, d, causal):
+    """Several heads; 8 heads take the per-XCD head mapping, 3 heads the plain one."""
+    q, k, v, do = _inputs(B, H, N, d, seed=2100 + H)
+    _check(fa, q, k, v, do, causal, default_scale(d), f"B={B} H={H} N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_long_sequence(fa, causal):
+    """N = 4096 at d = 128: 32 key tiles per dQ workgroup, 64 query tiles per dK/dV workgroup."""
+    q, k, v, do = _inputs(1, 2, 4096, 128, seed=2200 + causal)
+    _check(fa, q, k, v, do, causal, default_scale(128), f"N=4096 causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_wide_logits(fa, causal):
+    """Q, K ~ N(0, 4^2): sharply peaked rows, P close to one-hot."""
+    q, k, v, do = _inputs(1, 2, 300, 128, seed=2300 + causal, sigma_qk=4.0)
+    _check(fa, q, k, v, do, causal, default_scale(128), f"sigma 4 causal={causal}")
+
+
+def test_bwd_other_scale(fa):
+    q, k, v, do = _inputs(1, 2, 300, 64, seed=2400)
+    _check(fa, q, k, v, do, True, 0.3, "scale 0.3")
+
+
+def test_bwd_deterministic(fa):
+    """Every output element is reduced in a fixed order: repeated launches are bitwise identical."""
+    q, k, v, do = _inputs(2, 4, 777, 128, seed=2500)
+    a = _run(fa, q, k, v, do, True, default_scale(128))
+    for _ in range(3):
+        b = _run(fa, q, k, v, do, True, default_scale(128))
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_bwd_fp32_unsupported(fa):
+    q, k, v, do = (t.float().cuda() for t in _inputs(1, 1, 64, 64, seed=2600))
+    O, L = fa.forward(q, k, v, causal=False)
+    with pytest.raises(fa.FaError) as e:
+        fa.backward(q, k, v, O, L, do)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED

@@ -1,7 +1,8 @@
-"""Tiled online-softmax attention forward pass for MI355X (gfx950).
+"""Tiled online-softmax attention forward and backward passes for MI355X (gfx950).
 
-``fa_fwd`` mirrors the C entry point of ``libfa.so``; ``forward`` allocates the
-outputs and calls it. Importing fails loudly when the HIP library is not built.
+``fa_fwd`` and ``fa_bwd`` mirror the C entry points of ``libfa.so``; ``forward``
+and ``backward`` allocate the outputs (and the backward workspace) and call them.
+Importing fails loudly when the HIP library is not built.
 """
 
 from ._binding import (  # noqa: F401
@@ -14,9 +15,12 @@ from ._binding import (  # noqa: F401
     FA_OK,
     LIB_PATH,
     FaError,
+    backward,
+    fa_bwd,
     fa_fwd,
     fa_status_string,
     fa_version,
     forward,
+    raw_fa_bwd,
     raw_fa_fwd,
 )

@@ -1,6 +1,6 @@
 """ctypes binding of libfa.so: argument marshalling only.
 
-Every step of the attention forward pass runs in the HIP kernels of libfa.so; this
+Every step of the attention forward and backward passes runs in the HIP kernels of libfa.so; this
 module checks tensor metadata, passes raw device pointers, sizes and the stream
 handle, and turns status codes into exceptions. There is no fallback: if the
 library is missing, importing the package fails.
@@ -34,6 +34,11 @@ _lib.fa_fwd.argtypes = [
     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
     ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
 ]
+_lib.fa_bwd.restype = ctypes.c_int
+_lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
+    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+    ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_status_string.argtypes = [ctypes.c_int]
 _lib.fa_version.restype = ctypes.c_int
@@ -41,8 +46,8 @@ _lib.fa_version.argtypes = []
 
 
 class FaError(RuntimeError):
-    def __init__(self, status: int):
-        super().__init__(f"fa_fwd failed: {fa_status_string(status)} (status {status})")
+    def __init__(self, status: int, entry: str = "fa_fwd"):
+        super().__init__(f"{entry} failed: {fa_status_string(status)} (status {status})")
         self.status = status
 
 
@@ -57,6 +62,12 @@ def fa_version() -> int:
 def raw_fa_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, stream, dtype) -> int:
     """The C entry point with integer pointers; returns the status code."""
     return int(_lib.fa_fwd(Q, K, V, O, L, B, H, N, d, int(causal), float(scale), stream, int(dtype)))
+
+
+def raw_fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """The C backward entry point with integer pointers; returns the status code."""
+    return int(_lib.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, int(causal),
+                           float(scale), stream, int(dtype)))
 
 
 _DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
@@ -104,3 +115,56 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=No
     L = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, O, L, B, H, N, d, causal, scale, stream)
     return O, L
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return stream
+
+
+def fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, stream=None):
+    """Enqueue the backward pass on ``stream`` (default: torch's current stream).
+
+    Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d] device tensors of one dtype;
+    L: contiguous fp32 [B, H, N]; work: contiguous fp32 device tensor of at least
+    2*B*H*N elements. Raises FaError on a bad argument.
+    """
+    dt = Q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for t in (Q, K, V, O, dO, dQ, dK, dV):
+        if t.dtype != dt or tuple(t.shape) != (B, H, N, d) or not t.is_contiguous():
+            raise ValueError("Q, K, V, O, dO, dQ, dK, dV must be contiguous [B, H, N, d] tensors of one dtype")
+        if t.device.type != "cuda" or t.device != Q.device:
+            raise ValueError("all tensors must live on the same GPU")
+    if L.dtype != torch.float32 or tuple(L.shape) != (B, H, N) or not L.is_contiguous() or L.device != Q.device:
+        raise ValueError("L must be a contiguous fp32 [B, H, N] tensor on the same GPU")
+    if (work.dtype != torch.float32 or not work.is_contiguous() or work.device != Q.device
+            or work.numel() < 2 * B * H * N):
+        raise ValueError("work must be a contiguous fp32 tensor of 2*B*H*N elements on the same GPU")
+    st = raw_fa_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dO), _ptr(dQ), _ptr(dK),
+                    _ptr(dV), _ptr(work), B, H, N, d, causal, scale,
+                    _stream_handle(stream, Q.device), _DTYPES[dt])
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate dQ, dK, dV (like q) and the fp32 workspace, run fa_bwd, return (dQ, dK, dV).
+
+    ``o`` and ``lse`` are the outputs of ``forward(q, k, v, causal, scale)``.
+    """
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32).item())
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(q)
+    dv = torch.empty_like(q)
+    work = torch.empty(2 * B * H * N, dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, work, B, H, N, d, causal, scale, stream)
+    return dq, dk, dv

@@ -1,0 +1,462 @@
+// Backward pass of the tiled online-softmax attention for CDNA4 (gfx950).
+//
+// Given Q, K, V, the forward outputs O and L and the gradient dO of a loss
+// with respect to O, computes dQ, dK and dV of O = softmax(scale Q K^T) V
+// (keys after the query excluded when causal) without storing the N x N
+// probability matrix:
+//
+//  * The probabilities are recomputed tile by tile from the stored logsumexp,
+//    P = exp(S - L) ("FlashAttention-2 from PyTorch to Triton", section "What
+//    We Are Building": exp(S - m) / l = exp(S - m - log l) = exp(S - L)), in
+//    base 2 with log2 e folded into the scale as in the forward kernels.
+//  * The work is split into a dQ kernel and a dK/dV kernel, each owning its
+//    outputs outright, so no atomics are needed (the split the "Case Study:
+//    metal-flash-attention" page describes for that project's backward pass).
+//  * dS = P o (dP - D) with dP = dO V^T and D_i = sum_c dO[i][c] O[i][c]: the
+//    Jacobian of a row softmax applied to dP, using sum_j P[i][j] dP[i][j] =
+//    dO_i . sum_j P[i][j] V_j = dO_i . O_i. A preprocessing kernel forms D and
+//    the base-2 logsumexp L * log2 e once per row.
+//
+// gfx950 mapping (bf16; v_mfma_f32_32x32x16_bf16, fp32 accumulation; P and dS
+// rounded to bf16 only as MFMA operands):
+//  * dQ kernel: a workgroup of four waves owns 128 query rows (32 per wave)
+//    and streams 64-key tiles of K and V through LDS (double-buffered, LDS
+//    DMA). Q and dO stay in VGPRs as B operands of S^T = K Q^T and
+//    dP^T = V dO^T, so in the result a lane holds 16 keys of one query and L,
+//    D are per-lane scalars; dQ^T += K^T dS^T reads K transposed
+//    (ds_read_b64_tr_b16) from the same tile.
+//  * dK/dV kernel: a workgroup owns 128 keys (32 per wave) and streams 64-row
+//    tiles of Q and dO (with their L and D) through LDS. K and V stay in VGPRs
+//    as B operands of S = Q K^T and dP = dO V^T, so a lane holds 16 queries of
+//    one key; dV^T += dO^T P and dK^T += Q^T dS read dO and Q transposed.
+//  * Causal: the dQ kernel stops at the diagonal key tile, the dK/dV kernel
+//    starts at the diagonal query tile; only tiles that straddle the diagonal
+//    or the ragged end are masked.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa.h"
+#include "fa_device.h"
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kBwdRows = 128;  // query rows (dQ kernel) or keys (dK/dV kernel) per workgroup
+constexpr int kBwdTile = 64;   // streamed rows per LDS tile
+
+// One dword per lane from rsrc + voffset into LDS at `lds` (via M0) + 4 * lane
+// (buffer_load_dword ... lds); same M0 wait state as load_lds_share.
+__device__ __forceinline__ void load_lds_4(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+#endif
+}
+
+// Per-lane addressing of a 64-row bf16 tile laid out with swz_k (BfLayout).
+//  * row reads: lane (l32, hh) reads chunk 2cc + hh of row 32 blk + l32 at
+//    tile + 32 blk ROW + (row_base ^ 32 cc);
+//  * transposing reads (ds_read_b64_tr_b16): the 16-lane group g reads rows
+//    16 mm + 8 hi + 4 hh + (lane % 16) / 4 (+ 32 blk) at column bytes
+//    64 db + 32 (g % 2) + 8 (lane % 4), i.e. tile + (32 blk + 16 mm) ROW +
+//    (tr_base[hi] ^ 64 db). Each lane then holds 4 consecutive rows of column
+//    32 db + l32: rows 16 mm + 4 hh + 0..3 (hi = 0) and + 8 (hi = 1), the
+//    order in which the MFMA result layout lists a lane's 16 rows.
+template <class LY>
+struct TileAddr {
+  int row_base;
+  int tr_base[2];
+  __device__ TileAddr(int lane) {
+    const int l32 = lane % 32, hh = lane / 32;
+    row_base = l32 * LY::ROW + 16 * (hh ^ LY::swz_k(l32));
+    const int trow = 4 * hh + (lane % 16) / 4;
+    const int tcol = 32 * ((lane / 16) % 2) + 8 * (lane % 4);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 8 * hi + trow;
+      tr_base[hi] = r * LY::ROW + 16 * ((tcol >> 4) ^ LY::swz_k(r)) + (tcol & 15);
+    }
+  }
+  __device__ bf16x8 row(const char *tile, int blk, int cc) const {
+    return *(const bf16x8 *)(tile + 32 * blk * LY::ROW + (row_base ^ (32 * cc)));
+  }
+  __device__ bf16x8 tr(const char *tile, int blk, int mm, int db) const {
+    const char *p = tile + (32 * blk + 16 * mm) * LY::ROW;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + (tr_base[0] ^ (64 * db))));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + (tr_base[1] ^ (64 * db))));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+// Per-lane global byte offsets of this wave's share of a 64-row tile load (LDS
+// slot p = 1024 gi + 16 lane holds chunk slot ^ swz_k(row) of row p / ROW);
+// load i adds 1024 i through its instruction offset, so it is taken out here.
+template <class LY>
+__device__ __forceinline__ void tile_load_offsets(int wave, int lane, int (&vo)[LY::LPW]) {
+#pragma unroll
+  for (int i = 0; i < LY::LPW; ++i) {
+    const int p = 64 * (wave * LY::LPW + i) + lane;
+    const int r = p / LY::CPR, j = p % LY::CPR;
+    vo[i] = r * LY::ROW + 16 * (j ^ LY::swz_k(r)) - 1024 * i;
+  }
+}
+
+// D[r] = sum_c dO[r][c] O[r][c] and L2[r] = L[r] log2 e for every row r of all
+// heads; work = [D (rows floats) | L2 (rows floats)].
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_prep_bf16_kernel(const bf16 *__restrict__ O,
+                                                               const bf16 *__restrict__ dO,
+                                                               const float *__restrict__ L,
+                                                               float *__restrict__ work, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const bf16 *o = O + r * D;
+  const bf16 *g = dO + r * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    const bf16x8 a = *(const bf16x8 *)(o + c);
+    const bf16x8 b = *(const bf16x8 *)(g + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+  }
+  work[r] = acc;
+  work[rows + r] = L[r] * kLog2e;
+}
+
+// dQ = scale * dS K for 128 query rows of one head.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
+    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+    const bf16 *__restrict__ dO, const float *__restrict__ work, bf16 *__restrict__ dQ, int N,
+    int n_qtiles, int64_t rows, float c, float scale) {
+  using LY = BfLayout<D, kBwdTile, 4>;
+  constexpr int BN = kBwdTile;
+  constexpr int NKB = BN / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NCC = D / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * LY::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int l32 = lane % 32, hh = lane / 32;
+
+  int bh, qt;
+  map_block(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, bh, qt);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const bf16 *Kh = K + head;
+  const bf16 *Vh = V + head;
+  const int q0 = qt * kBwdRows;
+  const int qw = q0 + kRowsPerWave * wave;
+  const int qrow = qw + l32;
+  const bool row_ok = qrow < N;
+
+  // Q and dO rows as the B operands of S^T = K Q^T and dP^T = V dO^T.
+  bf16x8 qf[NCC], gf[NCC];
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) {
+    const size_t off = head + (size_t)qrow * D + 16 * cc + 8 * hh;
+    qf[cc] = row_ok ? *(const bf16x8 *)(Q + off) : bf16x8{};
+    gf[cc] = row_ok ? *(const bf16x8 *)(dO + off) : bf16x8{};
+  }
+  const float l2 = row_ok ? work[rows + (size_t)bh * N + qrow] : 0.f;
+  const float dd = row_ok ? work[(size_t)bh * N + qrow] : 0.f;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  const TileAddr<LY> ta(lane);
+  int vo[LY::LPW];
+  tile_load_offsets<LY>(wave, lane, vo);
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int t) {
+    const int k0 = t * BN;
+    const int bytes = min(N - k0, BN) * LY::ROW;
+    const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + 1024 * wave * LY::LPW;
+    load_lds_share(make_rsrc(Kh + (size_t)k0 * D, bytes), dst, vo);
+    load_lds_share(make_rsrc(Vh + (size_t)k0 * D, bytes), dst + LY::TILE, vo);
+  };
+
+  const int kend = CAUSAL ? min(N, q0 + kBwdRows) : N;
+  const int nt = (kend + BN - 1) / BN;
+  issue(0);
+  for (int t = 0; t < nt; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t landed for every wave; every wave is done with tile t - 1
+    if (t + 1 < nt) issue(t + 1);
+    const char *ks = smem + (t & 1) * LY::STAGE;
+    const char *vs = ks + LY::TILE;
+    const int k0 = t * BN;
+
+    // S^T and dP^T blocks of 32 keys x 32 queries: lane (l32, hh), register r
+    // holds key k0 + 32 kb + 8 (r/4) + 4 hh + r%4 of query qrow.
+    f32x16 s[NKB], dp[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(ks, kb, cc), qf[cc], cc == 0 ? f32x16{} : s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(vs, kb, cc), gf[cc], cc == 0 ? f32x16{} : dp[kb], 0, 0, 0);
+      }
+    }
+    // P = exp2(S c - L2) (masked: 0) and dS = P (dP - D), as bf16 B operands.
+    const bool edge = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw);
+    bf16x8 dsb[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2_fast(fmaf(s[kb][r], c, -l2));
+        if (edge) {
+          const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+          if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+        }
+        dsb[kb][r / 8][r % 8] = (bf16)(p * (dp[kb][r] - dd));
+      }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(ks, kb, mm, db), dsb[kb][mm], acc[db], 0, 0, 0);
+  }
+
+  // Lane (l32, hh) holds dQ^T[32 db + 8 g + 4 hh + e][qrow] in acc[db][4 g + e].
+  if (row_ok) {
+    bf16 *out = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][4 * g + e] * scale);
+        *(bf16x4 *)(out + 32 * db + 8 * g + 4 * hh) = v4;
+      }
+  }
+}
+
+// dK = scale * dS^T Q and dV = P^T dO for 128 keys of one head.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
+    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+    const bf16 *__restrict__ dO, const float *__restrict__ work, bf16 *__restrict__ dK,
+    bf16 *__restrict__ dV, int N, int n_ktiles, int64_t rows, float c, float scale) {
+  using LY = BfLayout<D, kBwdTile, 4>;
+  constexpr int BQ = kBwdTile;
+  constexpr int NQB = BQ / 32;
+  constexpr int NDB = D / 32;
+  constexpr int NCC = D / 16;
+  constexpr int STAGE = 2 * LY::TILE + 2 * BQ * 4;  // Q tile, dO tile, L2, D
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int l32 = lane % 32, hh = lane / 32;
+
+  // Key tiles in ascending order: when causal, the first ones see the most queries.
+  int bh, kt;
+  map_block(blockIdx.x, gridDim.x, n_ktiles, false, bh, kt);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const bf16 *Qh = Q + head;
+  const bf16 *Gh = dO + head;
+  const float *Dh = work + (size_t)bh * N;
+  const float *L2h = work + rows + (size_t)bh * N;
+  const int k0 = kt * kBwdRows;
+  const int kw = k0 + kRowsPerWave * wave;
+  const int krow = kw + l32;
+  const bool row_ok = krow < N;
+
+  // K and V rows as the B operands of S = Q K^T and dP = dO V^T.
+  bf16x8 kf[NCC], vf[NCC];
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) {
+    const size_t off = head + (size_t)krow * D + 16 * cc + 8 * hh;
+    kf[cc] = row_ok ? *(const bf16x8 *)(K + off) : bf16x8{};
+    vf[cc] = row_ok ? *(const bf16x8 *)(V + off) : bf16x8{};
+  }
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const TileAddr<LY> ta(lane);
+  int vo[LY::LPW];
+  tile_load_offsets<LY>(wave, lane, vo);
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int t) {
+    const int qa = t * BQ;
+    const int n_ok = min(N - qa, BQ);
+    const uint32_t dst = smem_lds + (t & 1) * STAGE;
+    load_lds_share(make_rsrc(Qh + (size_t)qa * D, n_ok * LY::ROW), dst + 1024 * wave * LY::LPW, vo);
+    load_lds_share(make_rsrc(Gh + (size_t)qa * D, n_ok * LY::ROW), dst + LY::TILE + 1024 * wave * LY::LPW, vo);
+    if (wave == 0) load_lds_4(make_rsrc(L2h + qa, n_ok * 4), dst + 2 * LY::TILE, 4 * lane);
+    if (wave == 1) load_lds_4(make_rsrc(Dh + qa, n_ok * 4), dst + 2 * LY::TILE + BQ * 4, 4 * lane);
+  };
+
+  const int t_first = CAUSAL ? k0 / BQ : 0;
+  const int nt = (N + BQ - 1) / BQ;
+  issue(t_first);
+  for (int t = t_first; t < nt; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t landed for every wave; every wave is done with tile t - 1
+    if (t + 1 < nt) issue(t + 1);
+    const char *qs = smem + (t & 1) * STAGE;
+    const char *gs = qs + LY::TILE;
+    const float *ls = (const float *)(gs + LY::TILE);
+    const float *ds = ls + BQ;
+    const int q0 = t * BQ;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int qa = q0 + 32 * qb;  // first query of the block
+      // S and dP blocks of 32 queries x 32 keys: lane (l32, hh), register r
+      // holds query qa + 8 (r/4) + 4 hh + r%4 of key krow.
+      f32x16 s, dp;
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(qs, qb, cc), kf[cc], cc == 0 ? f32x16{} : s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(gs, qb, cc), vf[cc], cc == 0 ? f32x16{} : dp, 0, 0, 0);
+      }
+      const bool edge = (qa + 32 > N) || (CAUSAL && kw + 31 > qa);
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = 32 * qb + 8 * g + 4 * hh;  // local query of registers 4g .. 4g + 3
+        const f32x4 lq = *(const f32x4 *)(ls + qi);
+        const f32x4 dq = *(const f32x4 *)(ds + qi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = exp2_fast(fmaf(s[r], c, -lq[e]));
+          if (edge) {
+            const int query = q0 + qi + e;
+            if (query >= N || (CAUSAL && krow > query)) p = 0.f;
+          }
+          pb[r / 8][r % 8] = (bf16)p;
+          dsb[r / 8][r % 8] = (bf16)(p * (dp[r] - dq[e]));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS.
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(gs, qb, mm, db), pb[mm], dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(qs, qb, mm, db), dsb[mm], dk[db], 0, 0, 0);
+        }
+    }
+  }
+
+  // Lane (l32, hh) holds dV^T / dK^T[32 db + 8 g + 4 hh + e][krow] in [db][4 g + e].
+  if (row_ok) {
+    bf16 *ov = dV + head + (size_t)krow * D;
+    bf16 *ok = dK + head + (size_t)krow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 a4, b4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a4[e] = (bf16)dv[db][4 * g + e];
+          b4[e] = (bf16)(dk[db][4 * g + e] * scale);
+        }
+        *(bf16x4 *)(ov + 32 * db + 8 * g + 4 * hh) = a4;
+        *(bf16x4 *)(ok + 32 * db + 8 * g + 4 * hh) = b4;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
+                           const void *V, const void *O, const float *L, const void *dO, void *dQ,
+                           void *dK, void *dV, float *work, float c, float scale) {
+  const int64_t rows = BH * N;
+  const int ntiles = (N + kBwdRows - 1) / kBwdRows;
+  hipLaunchKernelGGL((fa_bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                     (const bf16 *)O, (const bf16 *)dO, L, work, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(256), 0, s,
+                     (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
+                     (bf16 *)dQ, N, ntiles, rows, c, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(256), 0, s,
+                     (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
+                     (bf16 *)dK, (bf16 *)dV, N, ntiles, rows, c, scale);
+  return hipGetLastError();
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const void *O,
+                              const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                              float *work, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                              float scale, void *stream, int dtype) {
+  if (!Q || !K || !V || !O || !L || !dO || !dQ || !dK || !dV || !work)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (N > (int64_t)1 << 24) return FA_ERR_UNSUPPORTED;
+  const int64_t ntiles = (N + kBwdRows - 1) / kBwdRows;
+  if (B * H > ((int64_t)1 << 31) / ntiles - 1) return FA_ERR_UNSUPPORTED;
+  if (B * H * N > ((int64_t)1 << 31) - 256) return FA_ERR_UNSUPPORTED;  // prep grid and row indices
+  const size_t esize = 2;
+  const size_t tbytes = (size_t)B * H * N * d * esize;
+  const size_t lbytes = (size_t)B * H * N * sizeof(float);
+  const void *ins[] = {Q, K, V, O, dO};
+  void *outs[] = {dQ, dK, dV};
+  for (void *o : outs) {
+    for (const void *i : ins)
+      if (overlaps(o, tbytes, i, tbytes)) return FA_ERR_INVALID_ARGUMENT;
+    if (overlaps(o, tbytes, L, lbytes) || overlaps(o, tbytes, work, 2 * lbytes))
+      return FA_ERR_INVALID_ARGUMENT;
+  }
+  if (overlaps(dQ, tbytes, dK, tbytes) || overlaps(dQ, tbytes, dV, tbytes) ||
+      overlaps(dK, tbytes, dV, tbytes))
+    return FA_ERR_INVALID_ARGUMENT;
+  for (const void *i : ins)
+    if (overlaps(work, 2 * lbytes, i, tbytes)) return FA_ERR_INVALID_ARGUMENT;
+  if (overlaps(work, 2 * lbytes, L, lbytes)) return FA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)L | (uintptr_t)dO |
+       (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV | (uintptr_t)work) & 15)
+    return FA_ERR_MISALIGNED;
+
+  const float c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
+  hipStream_t s = (hipStream_t)stream;
+  const int n = (int)N;
+  const int64_t BH = B * H;
+  hipError_t err;
+  if (d == 64)
+    err = causal ? launch_bwd_bf16<64, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
+                 : launch_bwd_bf16<64, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+  else
+    err = causal ? launch_bwd_bf16<128, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
+                 : launch_bwd_bf16<128, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}

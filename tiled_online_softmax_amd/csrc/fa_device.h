@@ -1,0 +1,140 @@
+// Device-side helpers shared by the forward and backward kernels of libfa.so
+// (gfx950). Internal to the library: included only by its .hip sources.
+#ifndef FA_DEVICE_H_
+#define FA_DEVICE_H_
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerWave = 32;  // query rows per wave (MFMA N dimension)
+constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr float kLn2 = 0.69314718055994530942f;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by the partner lane in the other half-wave (lane ^ 32), combined.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroup index -> (head, query tile). Workgroups are dispatched to the
+// eight XCDs round-robin (XCD = bid % 8, in order bid / 8 within an XCD).
+// When the heads split evenly over the XCDs, XCD x takes heads
+// [x*hpx, (x+1)*hpx), so each head's K/V stays in one XCD's L2; within an XCD,
+// and globally otherwise, work is ordered by query tile, all heads at one
+// tile before the next. For causal attention the tiles run from the last
+// query tile (most key tiles) to the first, so the longest workgroups start
+// first and the short ones fill the tail.
+__device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bool causal,
+                                          int &bh, int &qt) {
+  const int n_heads = nblocks / n_qtiles;
+  int t;
+  if (n_heads % kNumXcd == 0) {
+    const int hpx = n_heads / kNumXcd;
+    const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+    t = slot / hpx;
+    bh = xcd * hpx + slot % hpx;
+  } else {
+    t = bid / n_heads;
+    bh = bid % n_heads;
+  }
+  qt = causal ? (n_qtiles - 1 - t) : t;
+}
+
+// Layout of a bf16 tile of BN rows x D columns staged in LDS (rows of K, V, Q
+// or dO). Rows are written by LDS DMA in 1 KiB wave instructions; inside a row
+// the 16-byte chunks are XOR-permuted by one of two row functions, chosen per
+// tile by how it is read:
+//  * swz_k, for ds_read_b128 of 32 consecutive rows at one chunk: spreads 16
+//    consecutive rows over the 16 slots of a 256-byte bank line;
+//  * swz_v, for ds_read_b64_tr_b16 (a 16-lane group reads 4 consecutive rows x
+//    32 bytes and its partner group the next 32 bytes): 4 * (row index within
+//    the group of 4), so the 4 x 4 chunks of a group pair land in 16 slots.
+template <int D, int BN, int NW>
+struct BfLayout {
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int RPB = 16 / CPR;             // rows per 256-byte bank line
+  static constexpr int ROW = D * 2;                // bytes per row
+  static constexpr int TILE = BN * ROW;            // bytes per K (or V) tile
+  static constexpr int STAGE = 2 * TILE;           // K tile then V tile
+  static constexpr int LOADS = TILE / 1024;        // wave instructions per tile matrix
+  static constexpr int LPW = LOADS / NW;           // ... per wave
+  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
+  static_assert(BN % 32 == 0, "key tile is a multiple of the 32-key MFMA block");
+  __device__ static constexpr int swz_k(int r) { return (r / RPB) & (CPR - 1); }
+  __device__ static constexpr int swz_v(int r) { return 4 * ((r / RPB) & (4 / RPB - 1)); }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled; reads past the
+// end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// One wave's share of a tile matrix, LPW x buffer_load_dwordx4 ... lds: load i
+// moves 16 bytes per lane from rsrc + vo[i] + 1024 i into LDS at byte address
+// `lds` (via M0) + 1024 i + 16 * lane. The instruction offset (1024 i) is added
+// to both the buffer offset, inside the range check, and the LDS address, so
+// M0 is written once per share. Written as inline assembly so that the
+// compiler does not treat every later LDS read as possibly aliasing these
+// asynchronous writes (it would wait for the next tile's loads before reading
+// the current one); the kernel publishes the data itself with s_waitcnt
+// vmcnt(0) and a workgroup barrier. M0 is used by nothing else here.
+// On GFX9-family GPUs an LDS DMA must not read M0 in the instruction right
+// after the SALU write of M0: without the wait state (s_nop 0) the load can
+// still see the previous M0 and land in the previous share's slots.
+// The host compilation pass of the kernel templates never calls it.
+template <int LPW>
+__device__ __forceinline__ void load_lds_share(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, const int (&vo)[LPW]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(LPW == 2 || LPW == 4, "one wave issues 2 or 4 loads per tile matrix");
+  if constexpr (LPW == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds"
+                 :
+                 : "s"(lds), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(rsrc)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+                 :
+                 : "s"(lds), "v"(vo[0]), "v"(vo[1]), "s"(rsrc)
+                 : "memory", "m0");
+#endif
+}
+
+}  // namespace
+
+#endif  // FA_DEVICE_H_
