@@ -11,6 +11,11 @@ MFMA peak; ``traffic`` is the HBM traffic measured by rocprofv3 counters for the
 same kernel source (null when the kernel source has changed since). The CPU
 baseline times the fp64 oracle on a bounded sample of query rows on the host cores
 (on the GPU machine), and checks the sampled rows of the GPU output against it.
+
+``--pass bwd`` times the backward pass instead (one fa_bwd call: the preprocessing,
+dQ and dK/dV kernels) on the same workload with a seeded dO, with algorithmic
+FLOP = 8 d per admissible pair (the products dV = P^T dO, dP = dO V^T, dQ = dS K and
+dK = dS^T Q), and times the fp64 backward oracle on one head for the CPU baseline.
 """
 
 from __future__ import annotations
@@ -27,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16, causal, B4 H16 N4096 d128)"
+METRIC_BWD = "attn bwd TFLOP/s & % MFMA peak (bf16, causal, B4 H16 N4096 d128)"
 # MI355X published dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU;
 # fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
@@ -91,6 +97,34 @@ def cpu_baseline(w, q, k, v, O, L, target_s: float):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, do, dQ, dK, dV):
+    """Time the backward oracle on the first head (all rows: dK and dV need every
+    query); check that head of the GPU gradients against it."""
+    import numpy as np
+
+    import oracle
+
+    sl = (slice(0, 1), slice(0, 1))
+    args = [t[sl].double().numpy() for t in (q, k, v, do)]
+    t0 = time.perf_counter()
+    ref = oracle.attention_bwd(*args, w.causal, w.scale)
+    t = time.perf_counter() - t0
+    flops = 8.0 * w.d * float(w.pairs())
+    errs = {}
+    for name, g, r in zip(("dQ", "dK", "dV"), (dQ, dK, dV), ref):
+        a = g[sl].double().cpu().numpy()
+        errs[name] = float(np.max(np.abs(a - r)))
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"head (0, 0) of {w.B * w.H}, every row (full N x N S, P, dP, dS in fp64), {t:.1f} s",
+        "seconds": t,
+        "sampled_head_max_abs_err": errs,
+    }
+
+
 def copy_calibration(mib: int):
     """Three device-to-device copies of a known size: each reads and writes `mib` MiB.
 
@@ -118,6 +152,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the causal bf16 B4 H16 N4096 d128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run three plain device copies of MIB MiB each "
                          "(reference dispatches for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -145,8 +181,19 @@ def main():
     L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    if args.which == "bwd":
         fa.fa_fwd(qd, kd, vd, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+        g = torch.Generator().manual_seed(1000 + w.seed)
+        do = torch.randn((w.B, w.H, w.N, w.d), generator=g).to(q.dtype)
+        dod = do.to(dev)
+        dQ, dK, dV = (torch.empty_like(qd) for _ in range(3))
+        work = torch.empty(2 * w.B * w.H * w.N, dtype=torch.float32, device=dev)
+
+        def step():
+            fa.fa_bwd(qd, kd, vd, O, L, dod, dQ, dK, dV, work, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+    else:
+        def step():
+            fa.fa_fwd(qd, kd, vd, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
 
     for _ in range(args.warmup):
         step()
@@ -172,14 +219,18 @@ def main():
     ms_per_step = total_ms / args.steps
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
 
-    flops = w.flops()
+    bwd = args.which == "bwd"
+    flops = 2 * w.flops() if bwd else w.flops()  # backward: 8 d per pair
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(w.name)
+    traffic = None if bwd else measured_traffic(w.name)
+    # backward: Q, K, V, O, dO read and dQ, dK, dV written once, plus L
+    n_rows = w.B * w.H * w.N
+    io_bytes = (2 * (w.io_bytes() - 4 * n_rows) + 4 * n_rows) if bwd else w.io_bytes()
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -204,13 +255,16 @@ def main():
             "kernel_ms": {"avg": round(avg_launch_ms, 5), "median": round(launch_ms[len(launch_ms) // 2], 5),
                           "min": round(launch_ms[0], 5), "max": round(launch_ms[-1], 5)},
             "algorithmic_flop_per_launch": flops,
-            "algorithmic_bytes_per_launch": w.io_bytes(),
+            "algorithmic_bytes_per_launch": io_bytes,
         },
         "wall_s_timed": round(t_wall, 4),
         "cpu_baseline": None,
     }
+    if bwd:
+        rec["roofline"]["kernel_ms"]["covers"] = "one fa_bwd call: preprocessing, dQ and dK/dV kernels"
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, O, L, args.cpu_seconds)
+        rec["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do, dQ, dK, dV) if bwd
+                               else cpu_baseline(w, q, k, v, O, L, args.cpu_seconds))
     print(json.dumps(rec), flush=True)
 
 

@@ -110,26 +110,31 @@ __device__ __forceinline__ void tile_load_offsets(int wave, int lane, int (&vo)[
 }
 
 // D[r] = sum_c dO[r][c] O[r][c] and L2[r] = L[r] log2 e for every row r of all
-// heads; work = [D (rows floats) | L2 (rows floats)].
+// heads; work = [D (rows floats) | L2 (rows floats)]. D / 8 consecutive lanes
+// read one row, 16 bytes each (whole rows per wave instruction), and their
+// partial sums are combined by a fixed butterfly of lane exchanges.
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_prep_bf16_kernel(const bf16 *__restrict__ O,
                                                                const bf16 *__restrict__ dO,
                                                                const float *__restrict__ L,
                                                                float *__restrict__ work, int64_t rows) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const bf16 *o = O + r * D;
-  const bf16 *g = dO + r * D;
+  constexpr int LPR = D / 8;    // lanes per row
+  constexpr int RPB = 256 / LPR;  // rows per workgroup
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D; c += 8) {
-    const bf16x8 a = *(const bf16x8 *)(o + c);
-    const bf16x8 b = *(const bf16x8 *)(g + c);
+  if (r < rows) {
+    const bf16x8 a = *(const bf16x8 *)(O + r * D + 8 * part);
+    const bf16x8 b = *(const bf16x8 *)(dO + r * D + 8 * part);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
   }
-  work[r] = acc;
-  work[rows + r] = L[r] * kLog2e;
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off);
+  if (r < rows && part == 0) {
+    work[r] = acc;
+    work[rows + r] = L[r] * kLog2e;
+  }
 }
 
 // dQ = scale * dS K for 128 query rows of one head.
@@ -210,19 +215,24 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
       }
     }
     // P = exp2(S c - L2) (masked: 0) and dS = P (dP - D), as bf16 B operands.
-    const bool edge = (k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw);
     bf16x8 dsb[NKB][2];
+    auto probs = [&](auto edge_tag) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2_fast(fmaf(s[kb][r], c, -l2));
-        if (edge) {
-          const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-          if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_fast(fmaf(s[kb][r], c, -l2));
+          if constexpr (decltype(edge_tag)::value) {
+            const int key = k0 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+            if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+          }
+          dsb[kb][r / 8][r % 8] = (bf16)(p * (dp[kb][r] - dd));
         }
-        dsb[kb][r / 8][r % 8] = (bf16)(p * (dp[kb][r] - dd));
-      }
+    };
+    if ((k0 + BN > N) || (CAUSAL && k0 + BN - 1 > qw))
+      probs(std::true_type{});
+    else
+      probs(std::false_type{});
     // dQ^T += K^T dS^T.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -322,18 +332,18 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
     const float *ls = (const float *)(gs + LY::TILE);
     const float *ds = ls + BQ;
     const int q0 = t * BQ;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qa = q0 + 32 * qb;  // first query of the block
-      // S and dP blocks of 32 queries x 32 keys: lane (l32, hh), register r
-      // holds query qa + 8 (r/4) + 4 hh + r%4 of key krow.
+    // One block of 32 queries (q0 + 32 qb ..): S and dP blocks of 32 queries x
+    // 32 keys (lane (l32, hh), register r holds query 32 qb + 8 (r/4) + 4 hh +
+    // r%4 of the tile, key krow), P and dS, then dV^T += dO^T P and
+    // dK^T += Q^T dS. EDGE: test every element against N and the causal rule.
+    auto block = [&](int qb, auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
       f32x16 s, dp;
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(qs, qb, cc), kf[cc], cc == 0 ? f32x16{} : s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(gs, qb, cc), vf[cc], cc == 0 ? f32x16{} : dp, 0, 0, 0);
       }
-      const bool edge = (qa + 32 > N) || (CAUSAL && kw + 31 > qa);
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           float p = exp2_fast(fmaf(s[r], c, -lq[e]));
-          if (edge) {
+          if constexpr (EDGE) {
             const int query = q0 + qi + e;
             if (query >= N || (CAUSAL && krow > query)) p = 0.f;
           }
@@ -352,7 +362,6 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
           dsb[r / 8][r % 8] = (bf16)(p * (dp[r] - dq[e]));
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS.
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
@@ -360,6 +369,14 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(gs, qb, mm, db), pb[mm], dv[db], 0, 0, 0);
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(qs, qb, mm, db), dsb[mm], dk[db], 0, 0, 0);
         }
+    };
+    // Masks only on tiles with a query past N or before one of this wave's keys.
+    if ((q0 + BQ > N) || (CAUSAL && kw + 31 > q0)) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) block(qb, std::true_type{});
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) block(qb, std::false_type{});
     }
   }
 
@@ -389,7 +406,8 @@ hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, cons
                            void *dK, void *dV, float *work, float c, float scale) {
   const int64_t rows = BH * N;
   const int ntiles = (N + kBwdRows - 1) / kBwdRows;
-  hipLaunchKernelGGL((fa_bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+  constexpr int prep_rows = 256 / (D / 8);
+  hipLaunchKernelGGL((fa_bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + prep_rows - 1) / prep_rows)), dim3(256), 0, s,
                      (const bf16 *)O, (const bf16 *)dO, L, work, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
