@@ -25,10 +25,12 @@
 //    dP^T = V dO^T, so in the result a lane holds 16 keys of one query and L,
 //    D are per-lane scalars; dQ^T += K^T dS^T reads K transposed
 //    (ds_read_b64_tr_b16) from the same tile.
-//  * dK/dV kernel: a workgroup owns 128 keys (32 per wave) and streams 64-row
-//    tiles of Q and dO (with their L and D) through LDS. K and V stay in VGPRs
-//    as B operands of S = Q K^T and dP = dO V^T, so a lane holds 16 queries of
-//    one key; dV^T += dO^T P and dK^T += Q^T dS read dO and Q transposed.
+//  * dK/dV kernel: a workgroup of eight waves owns 128 keys and streams
+//    64-row tiles of Q and dO (with their L and D) through LDS; wave w takes
+//    keys 32 (w % 4) .. and query block w / 4 of each tile. K and V of the 128
+//    keys stay in LDS as B operands of S = Q K^T and dP = dO V^T, so a lane
+//    holds 16 queries of one key; dV^T += dO^T P and dK^T += Q^T dS read dO and
+//    Q transposed. The two query-block halves are summed at the end.
 //  * Causal: the dQ kernel stops at the diagonal key tile, the dK/dV kernel
 //    starts at the diagonal query tile; only tiles that straddle the diagonal
 //    or the ragged end are masked.
@@ -258,24 +260,37 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
   }
 }
 
-// dK = scale * dS^T Q and dV = P^T dO for 128 keys of one head.
+// dK = scale * dS^T Q and dV = P^T dO for 128 keys of one head. Eight waves:
+// wave w owns keys 32 (w % 4) .. + 31 of the workgroup and query block w / 4
+// (32 rows) of every 64-row tile, so two waves share a SIMD; K and V of the
+// 128 keys stay in LDS for the whole loop and are read there as B operands,
+// which keeps a wave's registers to its two accumulators. At the end the two
+// waves of a key block add their partial dK, dV through LDS (block 0 + block
+// 1, a fixed order).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_bf16_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ work, bf16 *__restrict__ dK,
     bf16 *__restrict__ dV, int N, int n_ktiles, int64_t rows, float c, float scale) {
-  using LY = BfLayout<D, kBwdTile, 4>;
+  constexpr int NW = 8;
+  using LY = BfLayout<D, kBwdTile, NW>;   // streamed Q, dO tiles
+  using LK = BfLayout<D, kBwdRows, NW>;   // the workgroup's K, V rows
   constexpr int BQ = kBwdTile;
-  constexpr int NQB = BQ / 32;
   constexpr int NDB = D / 32;
   constexpr int NCC = D / 16;
+  constexpr int KV = 2 * LK::TILE;                  // K then V
   constexpr int STAGE = 2 * LY::TILE + 2 * BQ * 4;  // Q tile, dO tile, L2, D
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int PART = 2 * NDB * 16 * 64 * 4;       // one wave's partial dK, dV
+  constexpr int SMEM = (KV + 2 * STAGE > 4 * PART) ? KV + 2 * STAGE : 4 * PART;
+  static_assert(SMEM <= 160 * 1024, "LDS budget of a CU");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
-  const int l32 = lane % 32, hh = lane / 32;
+  const int hh = lane / 32;
+  const int kb = wave % 4;  // key block of this wave
+  const int qb = wave / 4;  // query block of every tile
 
   // Key tiles in ascending order: when causal, the first ones see the most queries.
   int bh, kt;
@@ -286,17 +301,19 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
   const float *Dh = work + (size_t)bh * N;
   const float *L2h = work + rows + (size_t)bh * N;
   const int k0 = kt * kBwdRows;
-  const int kw = k0 + kRowsPerWave * wave;
-  const int krow = kw + l32;
-  const bool row_ok = krow < N;
+  const int kw = k0 + kRowsPerWave * kb;  // first key of this wave
+  const int krow = kw + lane % 32;
 
-  // K and V rows as the B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[NCC], vf[NCC];
-#pragma unroll
-  for (int cc = 0; cc < NCC; ++cc) {
-    const size_t off = head + (size_t)krow * D + 16 * cc + 8 * hh;
-    kf[cc] = row_ok ? *(const bf16x8 *)(K + off) : bf16x8{};
-    vf[cc] = row_ok ? *(const bf16x8 *)(V + off) : bf16x8{};
+  const uint32_t smem_lds = lds_addr(smem);
+  const char *ks = smem;
+  const char *vs = smem + LK::TILE;
+  {
+    int vk[LK::LPW];
+    tile_load_offsets<LK>(wave, lane, vk);
+    const int bytes = min(N - k0, kBwdRows) * LK::ROW;
+    const uint32_t dst = smem_lds + 1024 * wave * LK::LPW;
+    load_lds_share(make_rsrc(K + head + (size_t)k0 * D, bytes), dst, vk);
+    load_lds_share(make_rsrc(V + head + (size_t)k0 * D, bytes), dst + LK::TILE, vk);
   }
 
   f32x16 dk[NDB], dv[NDB];
@@ -309,95 +326,118 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_bf16_kernel(
   const TileAddr<LY> ta(lane);
   int vo[LY::LPW];
   tile_load_offsets<LY>(wave, lane, vo);
-  const uint32_t smem_lds = lds_addr(smem);
   auto issue = [&](int t) {
     const int qa = t * BQ;
     const int n_ok = min(N - qa, BQ);
-    const uint32_t dst = smem_lds + (t & 1) * STAGE;
+    const uint32_t dst = smem_lds + KV + (t & 1) * STAGE;
     load_lds_share(make_rsrc(Qh + (size_t)qa * D, n_ok * LY::ROW), dst + 1024 * wave * LY::LPW, vo);
     load_lds_share(make_rsrc(Gh + (size_t)qa * D, n_ok * LY::ROW), dst + LY::TILE + 1024 * wave * LY::LPW, vo);
     if (wave == 0) load_lds_4(make_rsrc(L2h + qa, n_ok * 4), dst + 2 * LY::TILE, 4 * lane);
     if (wave == 1) load_lds_4(make_rsrc(Dh + qa, n_ok * 4), dst + 2 * LY::TILE + BQ * 4, 4 * lane);
   };
 
-  const int t_first = CAUSAL ? k0 / BQ : 0;
+  // Tile t: wait for it, start loading t + 1, and (unless every key of the
+  // wave lies after every query of its block) compute this wave's block: S
+  // and dP blocks of 32 queries x 32 keys (lane (l32, hh), register r holds
+  // query qa + 8 (r/4) + 4 hh + r%4 of key krow), P and dS (EDGE: test every
+  // element against N and the causal rule), dV^T += dO^T P, dK^T += Q^T dS.
   const int nt = (N + BQ - 1) / BQ;
-  issue(t_first);
-  for (int t = t_first; t < nt; ++t) {
+  auto iteration = [&](int t, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile t landed for every wave; every wave is done with tile t - 1
+    __syncthreads();  // tile t (and K, V) landed for every wave; every wave is done with tile t - 1
     if (t + 1 < nt) issue(t + 1);
-    const char *qs = smem + (t & 1) * STAGE;
+    const char *qs = smem + KV + (t & 1) * STAGE;
     const char *gs = qs + LY::TILE;
     const float *ls = (const float *)(gs + LY::TILE);
     const float *ds = ls + BQ;
-    const int q0 = t * BQ;
-    // One block of 32 queries (q0 + 32 qb ..): S and dP blocks of 32 queries x
-    // 32 keys (lane (l32, hh), register r holds query 32 qb + 8 (r/4) + 4 hh +
-    // r%4 of the tile, key krow), P and dS, then dV^T += dO^T P and
-    // dK^T += Q^T dS. EDGE: test every element against N and the causal rule.
-    auto block = [&](int qb, auto edge_tag) {
-      constexpr bool EDGE = decltype(edge_tag)::value;
-      f32x16 s, dp;
-#pragma unroll
-      for (int cc = 0; cc < NCC; ++cc) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(qs, qb, cc), kf[cc], cc == 0 ? f32x16{} : s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(gs, qb, cc), vf[cc], cc == 0 ? f32x16{} : dp, 0, 0, 0);
-      }
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = 32 * qb + 8 * g + 4 * hh;  // local query of registers 4g .. 4g + 3
-        const f32x4 lq = *(const f32x4 *)(ls + qi);
-        const f32x4 dq = *(const f32x4 *)(ds + qi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = exp2_fast(fmaf(s[r], c, -lq[e]));
-          if constexpr (EDGE) {
-            const int query = q0 + qi + e;
-            if (query >= N || (CAUSAL && krow > query)) p = 0.f;
-          }
-          pb[r / 8][r % 8] = (bf16)p;
-          dsb[r / 8][r % 8] = (bf16)(p * (dp[r] - dq[e]));
-        }
-      }
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(gs, qb, mm, db), pb[mm], dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(qs, qb, mm, db), dsb[mm], dk[db], 0, 0, 0);
-        }
-    };
-    // Masks only on tiles with a query past N or before one of this wave's keys.
-    if ((q0 + BQ > N) || (CAUSAL && kw + 31 > q0)) {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) block(qb, std::true_type{});
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) block(qb, std::false_type{});
-    }
-  }
+    const int qa = t * BQ + 32 * qb;  // first query of this wave's block
+    if (CAUSAL && EDGE && kw > qa + 31) return;  // every key of the wave after every query
 
-  // Lane (l32, hh) holds dV^T / dK^T[32 db + 8 g + 4 hh + e][krow] in [db][4 g + e].
-  if (row_ok) {
-    bf16 *ov = dV + head + (size_t)krow * D;
-    bf16 *ok = dK + head + (size_t)krow * D;
+    f32x16 s, dp;
+    // Each step's four operand reads stay next to its two MFMAs (the fence
+    // keeps the compiler from hoisting every read of the block into registers).
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(qs, qb, cc), ta.row(ks, kb, cc), cc == 0 ? f32x16{} : s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(gs, qb, cc), ta.row(vs, kb, cc), cc == 0 ? f32x16{} : dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int qi = 32 * qb + 8 * g + 4 * hh;  // local query of registers 4g .. 4g + 3
+      const f32x4 lq = *(const f32x4 *)(ls + qi);
+      const f32x4 dq = *(const f32x4 *)(ds + qi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float p = exp2_fast(fmaf(s[r], c, -lq[e]));
+        if constexpr (EDGE) {
+          const int query = t * BQ + qi + e;
+          if (query >= N || (CAUSAL && krow > query)) p = 0.f;
+        }
+        pb[r / 8][r % 8] = (bf16)p;
+        dsb[r / 8][r % 8] = (bf16)(p * (dp[r] - dq[e]));
+      }
+    }
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(gs, qb, mm, db), pb[mm], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(qs, qb, mm, db), dsb[mm], dk[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  // Three runs of tiles, so that the masked and unmasked forms are never live
+  // together: the tiles that straddle the diagonal (causal: queries of the
+  // workgroup's own 128 positions), the full tiles after them, and a ragged
+  // last tile.
+  const int t_first = CAUSAL ? k0 / BQ : 0;
+  const int t_diag = CAUSAL ? min(nt, t_first + kBwdRows / BQ) : t_first;
+  const int t_full = max(t_diag, N / BQ);
+  issue(t_first);
+  int t = t_first;
+  for (; t < t_diag; ++t) iteration(t, std::true_type{});
+  for (; t < t_full; ++t) iteration(t, std::false_type{});
+  for (; t < nt; ++t) iteration(t, std::true_type{});
+
+  // Merge the two query-block halves of each key block: qb = 1 waves park
+  // their partials in LDS as [register][lane] floats, qb = 0 waves add them.
+  __syncthreads();  // every wave is done with the K, V and tile LDS
+  float *part = (float *)smem + (size_t)kb * (PART / 4);
+  if (qb == 1) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 a4, b4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a4[e] = (bf16)dv[db][4 * g + e];
-          b4[e] = (bf16)(dk[db][4 * g + e] * scale);
-        }
-        *(bf16x4 *)(ov + 32 * db + 8 * g + 4 * hh) = a4;
-        *(bf16x4 *)(ok + 32 * db + 8 * g + 4 * hh) = b4;
+      for (int r = 0; r < 16; ++r) {
+        part[((2 * db) * 16 + r) * 64 + lane] = dk[db][r];
+        part[((2 * db + 1) * 16 + r) * 64 + lane] = dv[db][r];
       }
   }
+  __syncthreads();
+  if (qb == 1 || krow >= N) return;
+  // Lane (l32, hh) holds dV^T / dK^T[32 db + 8 g + 4 hh + e][krow] in [db][4 g + e].
+  bf16 *ov = dV + head + (size_t)krow * D;
+  bf16 *ok = dK + head + (size_t)krow * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 a4, b4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        const float kk = dk[db][r] + part[((2 * db) * 16 + r) * 64 + lane];
+        const float vv = dv[db][r] + part[((2 * db + 1) * 16 + r) * 64 + lane];
+        a4[e] = (bf16)vv;
+        b4[e] = (bf16)(kk * scale);
+      }
+      *(bf16x4 *)(ov + 32 * db + 8 * g + 4 * hh) = a4;
+      *(bf16x4 *)(ok + 32 * db + 8 * g + 4 * hh) = b4;
+    }
 }
 
 template <int D, bool CAUSAL>
@@ -416,7 +456,7 @@ hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, cons
                      (bf16 *)dQ, N, ntiles, rows, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(256), 0, s,
+  hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(512), 0, s,
                      (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
                      (bf16 *)dK, (bf16 *)dV, N, ntiles, rows, c, scale);
   return hipGetLastError();

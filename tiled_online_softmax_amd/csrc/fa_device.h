@@ -115,8 +115,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 template <int LPW>
 __device__ __forceinline__ void load_lds_share(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, const int (&vo)[LPW]) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(LPW == 2 || LPW == 4, "one wave issues 2 or 4 loads per tile matrix");
-  if constexpr (LPW == 4)
+  static_assert(LPW == 1 || LPW == 2 || LPW == 4, "one wave issues 1, 2 or 4 loads per tile matrix");
+  if constexpr (LPW == 1)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(vo[0]), "s"(rsrc)
+                 : "memory", "m0");
+  else if constexpr (LPW == 4)
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
                  "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
                  "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
