@@ -33,6 +33,12 @@ if ROOT not in sys.path:
 
 METRIC = "attn fwd TFLOP/s & % MFMA peak (bf16, causal, B4 H16 N4096 d128)"
 METRIC_BWD = "attn bwd TFLOP/s & % MFMA peak (bf16, causal, B4 H16 N4096 d128)"
+
+
+def metric_name(which: str, w) -> str:
+    """The metric string for a pass and workload (METRIC / METRIC_BWD for the default one)."""
+    mask = "causal" if w.causal else "non-causal"
+    return f"attn {which} TFLOP/s & % MFMA peak ({w.dtype}, {mask}, B{w.B} H{w.H} N{w.N} d{w.d})"
 # MI355X published dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU;
 # fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
@@ -230,7 +236,7 @@ def main():
     io_bytes = (2 * (w.io_bytes() - 4 * n_rows) + 4 * n_rows) if bwd else w.io_bytes()
 
     rec = {
-        "metric": METRIC_BWD if bwd else METRIC,
+        "metric": metric_name(args.which, w),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -91,11 +91,14 @@ fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void *O, float *
  *            sum over c of dO*O, then L * log2 e). Owned by the caller; its
  *            contents after the call carry no meaning.
  *   B,H,N,d, causal, scale, stream: as for fa_fwd.
- *   dtype    FA_DTYPE_BF16 (FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED).
+ *   dtype    FA_DTYPE_BF16 or FA_DTYPE_F32 (all of Q, K, V, O, dO and the
+ *            gradients in that type).
  *
  * dS = P o (dP - D) with dP = dO V^T and D_i = sum_c dO[i][c] O[i][c];
- * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO; accumulation in fp32, P and
- * dS rounded to bf16 as MFMA operands. Ownership, asynchrony and validation as
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO; accumulation in fp32. For
+ * bf16, P and dS are rounded to bf16 as MFMA operands; for fp32 every operand
+ * stays fp32. Each gradient element is summed in a fixed order, so repeated
+ * calls give bitwise identical results. Ownership, asynchrony and validation as
  * for fa_fwd: the library allocates no memory; on an error nothing is
  * enqueued and the outputs are untouched.
  */

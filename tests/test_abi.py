@@ -109,9 +109,15 @@ def test_bwd_bad_arguments(kw):
     assert call_bwd(**kw) == fa.FA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(dtype=fa.FA_DTYPE_F32), dict(N=(1 << 24) + 1)])
+@pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(N=(1 << 24) + 1),
+                                dict(d=96, dtype=fa.FA_DTYPE_F32)])
 def test_bwd_unsupported(kw):
     assert call_bwd(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_overlap_uses_element_size():
+    # 64 x 64 fp32 tensors span 16 KiB: dQ 12 KiB after Q overlaps it (as bf16 it would not).
+    assert call_bwd(dtype=fa.FA_DTYPE_F32, dQ=A + 12 * 1024) == fa.FA_ERR_INVALID_ARGUMENT
 
 
 @pytest.mark.parametrize("kw", [dict(dQ=2 * A + 64), dict(dK=6 * A), dict(dV=7 * A + 4096),

@@ -6,6 +6,14 @@ term of the gradient carries one more bf16 rounding of P or dS as an MFMA operan
 (<= 2^-9 relative). The forward's O, rounded to bf16, enters D = sum_c dO O. A budget
 of five units of 2^-9 (~1e-2) of the largest entry covers these; the measured errors
 are 2.5e-3 to 5e-3 of it.
+
+Tolerance (fp32): 2e-5 * max(1, max |dX_ref|). Every operand stays fp32, so the error
+comes from rounding: P = exp2(S c - L2) carries the forward's L error and the
+exponent's rounding (|S c| up to ~30 at sigma 4, so ~30 * 2^-24 ~ 2e-6 relative),
+dP - D cancels two sums of d products, each of size up to ~sqrt(d), and each gradient
+sums up to N such terms in fp32 (random-walk growth ~sqrt(N) 2^-24). The measured
+errors are 2e-7 to 2e-6 of the largest entry at sigma 1 (N up to 4100) and up to
+7.4e-6 at sigma 4, where |S c| is largest.
 """
 
 import numpy as np
@@ -17,7 +25,7 @@ from workloads import default_scale, make_qkv
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-2
+TOL = {"bf16": 1e-2, "f32": 2e-5}
 
 
 @pytest.fixture(scope="module")
@@ -28,10 +36,10 @@ def fa():
     return tiled_online_softmax_amd
 
 
-def _inputs(B, H, N, d, seed, sigma_qk=1.0):
-    q, k, v = make_qkv(B, H, N, d, "bf16", seed=seed, sigma_qk=sigma_qk)
+def _inputs(B, H, N, d, seed, sigma_qk=1.0, dtype="bf16"):
+    q, k, v = make_qkv(B, H, N, d, dtype, seed=seed, sigma_qk=sigma_qk)
     g = torch.Generator().manual_seed(seed + 1)
-    do = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    do = torch.randn((B, H, N, d), generator=g).to(q.dtype)
     return q, k, v, do
 
 
@@ -48,11 +56,12 @@ def _check(fa, q, k, v, do, causal, scale, label):
     got = _run(fa, q, k, v, do, causal, scale)
     ref = oracle.attention_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(),
                                do.double().numpy(), causal, scale)
+    tol = TOL["f32" if q.dtype == torch.float32 else "bf16"]
     for name, a, r in zip(("dQ", "dK", "dV"), got, ref):
         a = a.double().cpu().numpy()
         assert np.isfinite(a).all(), f"{label}: {name} not finite"
         err = float(np.abs(a - r).max())
-        bound = TOL * max(1.0, float(np.abs(r).max()))
+        bound = tol * max(1.0, float(np.abs(r).max()))
         print(f"[parity-bwd] {label} {name} max|err|={err:.3e} (tol {bound:.3e})", flush=True)
         assert err <= bound, f"{label}: {name} error {err} > {bound}"
 
@@ -95,9 +104,10 @@ def test_bwd_other_scale(fa):
     _check(fa, q, k, v, do, True, 0.3, "scale 0.3")
 
 
-def test_bwd_deterministic(fa):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_deterministic(fa, dtype):
     """Every output element is reduced in a fixed order: repeated launches are bitwise identical."""
-    q, k, v, do = _inputs(2, 4, 777, 128, seed=2500)
+    q, k, v, do = _inputs(2, 4, 777, 128, seed=2500, dtype=dtype)
     a = _run(fa, q, k, v, do, True, default_scale(128))
     for _ in range(3):
         b = _run(fa, q, k, v, do, True, default_scale(128))
@@ -105,9 +115,40 @@ def test_bwd_deterministic(fa):
             assert torch.equal(x, y)
 
 
-def test_bwd_fp32_unsupported(fa):
-    q, k, v, do = (t.float().cuda() for t in _inputs(1, 1, 64, 64, seed=2600))
-    O, L = fa.forward(q, k, v, causal=False)
-    with pytest.raises(fa.FaError) as e:
-        fa.backward(q, k, v, O, L, do)
-    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+# fp32: 32-row workgroups and tiles, so the edges sit at multiples of 32.
+EDGE_N_F32 = [1, 2, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 257]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", EDGE_N_F32)
+def test_bwd_f32_edge_sizes(fa, N, causal, d):
+    q, k, v, do = _inputs(1, 2, N, d, seed=2600 + N + d, dtype="f32")
+    _check(fa, q, k, v, do, causal, default_scale(d), f"f32 N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(2, 4, 300, 128, True), (1, 3, 1000, 64, False),
+                                             (1, 8, 200, 128, False), (1, 8, 450, 64, True)])
+def test_bwd_f32_heads(fa, B, H, N, d, causal):
+    """Several heads; 8 heads take the per-XCD head mapping, 3 heads the plain one."""
+    q, k, v, do = _inputs(B, H, N, d, seed=2700 + H, dtype="f32")
+    _check(fa, q, k, v, do, causal, default_scale(d), f"f32 B={B} H={H} N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_f32_long_sequence(fa, d):
+    """N = 4100: 129 tiles per workgroup (each wave takes every fourth), a ragged last one."""
+    q, k, v, do = _inputs(1, 1, 4100, d, seed=2800 + d, dtype="f32")
+    _check(fa, q, k, v, do, True, default_scale(d), f"f32 N=4100 d={d}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_f32_wide_logits(fa, causal):
+    """Q, K ~ N(0, 4^2): sharply peaked rows, P close to one-hot."""
+    q, k, v, do = _inputs(1, 2, 300, 128, seed=2900 + causal, sigma_qk=4.0, dtype="f32")
+    _check(fa, q, k, v, do, causal, default_scale(128), f"f32 sigma 4 causal={causal}")
+
+
+def test_bwd_f32_other_scale(fa):
+    q, k, v, do = _inputs(1, 2, 300, 64, seed=3000, dtype="f32")
+    _check(fa, q, k, v, do, False, 0.3, "f32 scale 0.3")

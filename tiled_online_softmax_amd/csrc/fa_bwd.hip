@@ -112,24 +112,26 @@ __device__ __forceinline__ void tile_load_offsets(int wave, int lane, int (&vo)[
 }
 
 // D[r] = sum_c dO[r][c] O[r][c] and L2[r] = L[r] log2 e for every row r of all
-// heads; work = [D (rows floats) | L2 (rows floats)]. D / 8 consecutive lanes
-// read one row, 16 bytes each (whole rows per wave instruction), and their
-// partial sums are combined by a fixed butterfly of lane exchanges.
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_prep_bf16_kernel(const bf16 *__restrict__ O,
-                                                               const bf16 *__restrict__ dO,
-                                                               const float *__restrict__ L,
-                                                               float *__restrict__ work, int64_t rows) {
-  constexpr int LPR = D / 8;    // lanes per row
-  constexpr int RPB = 256 / LPR;  // rows per workgroup
+// heads; work = [D (rows floats) | L2 (rows floats)]. Consecutive lanes read 16
+// bytes each of one row (whole rows per wave instruction), and their partial
+// sums are combined by a fixed butterfly of lane exchanges.
+template <class T, int D>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const T *__restrict__ O,
+                                                          const T *__restrict__ dO,
+                                                          const float *__restrict__ L,
+                                                          float *__restrict__ work, int64_t rows) {
+  constexpr int EPL = 16 / sizeof(T);  // elements per lane
+  constexpr int LPR = D / EPL;         // lanes per row
+  constexpr int RPB = 256 / LPR;       // rows per workgroup
+  typedef T vec __attribute__((ext_vector_type(EPL)));
   const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
   float acc = 0.f;
   if (r < rows) {
-    const bf16x8 a = *(const bf16x8 *)(O + r * D + 8 * part);
-    const bf16x8 b = *(const bf16x8 *)(dO + r * D + 8 * part);
+    const vec a = *(const vec *)(O + r * D + EPL * part);
+    const vec b = *(const vec *)(dO + r * D + EPL * part);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+    for (int e = 0; e < EPL; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off);
@@ -440,6 +442,342 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 (v_mfma_f32_32x32x2_f32). A workgroup of four waves owns 32 query rows
+// (dQ kernel) or 32 keys (dK/dV kernel) and its waves take every fourth
+// 32-row tile of the other side, so each wave forms a partial gradient that
+// the workgroup sums through LDS in wave order at the end. The workgroup's own
+// rows stay in LDS (row stride D + 4 floats, so 16 rows read at one column hit
+// distinct banks) and are read there as the shared operand of S and dP; the
+// streamed tiles go straight from memory into VGPRs, once in row layout (lane
+// l32 holds row l32, contraction over the head dimension) and once in the
+// layout of the gradient product (lane (l32, hh) holds rows 8 (r/4) + 4 hh +
+// r%4 at columns NDB l32 .. NDB l32 + NDB - 1, contraction over the rows). The
+// product then yields column NDB i + db of the gradient in row i of block db.
+constexpr int kF32Block = 32;  // rows per workgroup and per streamed tile (fp32)
+constexpr int kF32BwdWaves = 4;
+
+// scale * (sum over the waves' partials) into rows r0 .. r0 + 31 of `out`
+// (rows at or past N skipped). `acc` holds this wave's partial in the layout
+// the permuted-column products leave: lane (l32, hh), block db, register
+// 4 g + e hold row l32, column NDB (8 g + 4 hh + e) + db. `part` is LDS of
+// NW x 32 x (D + 4) floats; the caller has synchronised the workgroup before.
+template <int D, int NW>
+__device__ __forceinline__ void merge_store_f32(float *part, const f32x16 (&acc)[D / 32], int wave,
+                                                int tid, float *out, int r0, int N, float scale) {
+  constexpr int NDB = D / 32;
+  constexpr int OS = D + 4;
+  const int lane = tid % 64, l32 = lane % 32, hh = lane / 32;
+  float *orow = part + (wave * kF32Block + l32) * OS;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int h = 0; h < NDB; ++h) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * h + e;  // (column offset within the group) = e' NDB + db
+        v[e] = acc[idx % NDB][4 * g + idx / NDB];
+      }
+      *(f32x4 *)(orow + NDB * (8 * g + 4 * hh) + 4 * h) = v;
+    }
+  __syncthreads();
+  constexpr int C4 = D / 4;
+  static_assert(kF32Block * C4 % (NW * 64) == 0, "merge must split evenly over the workgroup");
+#pragma unroll
+  for (int it = 0; it < kF32Block * C4 / (NW * 64); ++it) {
+    const int idx = tid + NW * 64 * it;
+    const int row = idx / C4, c4 = idx % C4;
+    if (r0 + row >= N) continue;
+    f32x4 sum = *(const f32x4 *)(part + row * OS + 4 * c4);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) sum += *(const f32x4 *)(part + (w * kF32Block + row) * OS + 4 * c4);
+    *(f32x4 *)(out + (size_t)(r0 + row) * D + 4 * c4) = sum * scale;
+  }
+}
+
+// Rows r0 .. r0 + 31 of two row-major [N][D] fp32 arrays into LDS rows of
+// D + 4 floats (rows at or past N as zeros).
+template <int D, int NW>
+__device__ __forceinline__ void stage_rows_f32(float *dst, const float *a, const float *b, int r0,
+                                               int N, int tid) {
+  constexpr int ROW = D * 4;
+  constexpr int OS = D + 4;
+  constexpr int C4 = D / 4;
+  const int bytes = min(N - r0, kF32Block) * ROW;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + (size_t)r0 * D, bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + (size_t)r0 * D, bytes);
+#pragma unroll
+  for (int it = 0; it < kF32Block * C4 / (NW * 64); ++it) {
+    const int idx = tid + NW * 64 * it;
+    const int row = idx / C4, c4 = idx % C4;
+    *(f32x4 *)(dst + row * OS + 4 * c4) = F32Vec<4>::load(ra, row * ROW + 16 * c4);
+    *(f32x4 *)(dst + (kF32Block + row) * OS + 4 * c4) = F32Vec<4>::load(rb, row * ROW + 16 * c4);
+  }
+}
+
+// dQ = scale * dS K for 32 query rows of one head (fp32).
+//  S^T = K Q^T, dP^T = V dO^T: K, V tiles in row layout as A operands, the
+//  block's Q and dO rows from LDS as B operands; lane (l32, hh) then holds
+//  keys 8 (r/4) + 4 hh + r%4 of query l32, whose L2 and D are lane scalars.
+//  dQ^T += K^T dS^T with K in the gradient layout.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dq_f32_kernel(
+    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
+    const float *__restrict__ dO, const float *__restrict__ work, float *__restrict__ dQ, int N,
+    int n_qblocks, int64_t rows, float c, float scale) {
+  constexpr int NW = kF32BwdWaves;
+  constexpr int BQ = kF32Block, BN = kF32Block;
+  constexpr int HD = D / 2;
+  constexpr int NDB = D / 32;
+  constexpr int ROW = D * 4;
+  constexpr int OS = D + 4;
+  using VV = F32Vec<NDB>;
+  typedef typename VV::type vvec;
+  constexpr int OPND = 2 * BQ * OS;
+  constexpr int PART = NW * BQ * OS;
+  __shared__ __attribute__((aligned(16))) float smem[OPND > PART ? OPND : PART];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, l32 = lane % 32, hh = lane / 32;
+
+  int bh, qb;
+  map_block(blockIdx.x, gridDim.x, n_qblocks, CAUSAL, bh, qb);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const float *Kh = K + head;
+  const float *Vh = V + head;
+  const int q0 = qb * BQ;
+  const int qrow = q0 + l32;
+  const bool row_ok = qrow < N;
+
+  stage_rows_f32<D, NW>(smem, Q + head, dO + head, q0, N, tid);
+  const float l2 = row_ok ? work[rows + (size_t)bh * N + qrow] : 0.f;
+  const float dd = row_ok ? work[(size_t)bh * N + qrow] : 0.f;
+  __syncthreads();
+  const float *qs = smem + l32 * OS + hh * HD;
+  const float *gs = smem + (BQ + l32) * OS + hh * HD;
+
+  const int kend = CAUSAL ? min(N, q0 + BQ) : N;
+  const int nt = (kend + BN - 1) / BN;
+
+  f32x4 kf[HD / 4], vf[HD / 4];
+  vvec kg[16];
+  auto tile_rsrc = [&](const float *base, int t) {
+    const int k0 = t * BN;
+    return make_rsrc(base + (size_t)k0 * D, min(N - k0, BN) * ROW);
+  };
+  auto load_rows = [&](f32x4 (&dst)[HD / 4], const float *base, int t) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, t);
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) dst[j] = F32Vec<4>::load(r, l32 * ROW + hh * HD * 4 + 16 * j);
+  };
+  auto load_grad = [&](vvec (&dst)[16], const float *base, int t) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[i] = VV::load(r, (8 * (i / 4) + 4 * hh + i % 4) * ROW + NDB * 4 * l32);
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  if (wave < nt) {
+    load_rows(kf, Kh, wave);
+    load_rows(vf, Vh, wave);
+  }
+  for (int t = wave; t < nt; t += NW) {
+    const int k0 = t * BN;
+    const bool more = t + NW < nt;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) {
+      const f32x4 b = *(const f32x4 *)(qs + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[j][e], b[e], s, 0, 0, 0);
+    }
+    // The fences keep each load where the registers it fills have been freed.
+    __builtin_amdgcn_sched_barrier(0);
+    load_grad(kg, Kh, t);
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) {
+      const f32x4 b = *(const f32x4 *)(gs + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[j][e], b[e], dp, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_rows(kf, Kh, t + NW);
+    __builtin_amdgcn_sched_barrier(0);
+    // dS^T = P^T o (dP^T - D); keys past N and (causal) after the query give P = 0.
+    const bool edge = k0 + BN > N || (CAUSAL && k0 + BN > q0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = exp2_fast(fmaf(s[r], c, -l2));
+      if (edge) {
+        const int key = k0 + 8 * (r / 4) + 4 * hh + r % 4;
+        if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+      }
+      s[r] = p * (dp[r] - dd);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kg[r][db], s[r], acc[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_rows(vf, Vh, t + NW);
+    // Keep the accumulators in AGPRs across iterations.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+a"(acc[db]));
+  }
+
+  __syncthreads();  // every wave is done with the Q, dO rows in LDS
+  merge_store_f32<D, NW>(smem, acc, wave, tid, dQ + head, q0, N, scale);
+}
+
+// dK = scale * dS^T Q and dV = P^T dO for 32 keys of one head (fp32).
+//  S = Q K^T, dP = dO V^T: Q, dO tiles in row layout as A operands, the
+//  block's K and V rows from LDS as B operands; lane (l32, hh) then holds
+//  queries 8 (r/4) + 4 hh + r%4 of key l32. dV^T += dO^T P and dK^T += Q^T dS
+//  with dO and Q in the gradient layout.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_f32_kernel(
+    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
+    const float *__restrict__ dO, const float *__restrict__ work, float *__restrict__ dK,
+    float *__restrict__ dV, int N, int n_kblocks, int64_t rows, float c, float scale) {
+  constexpr int NW = kF32BwdWaves;
+  constexpr int BQ = kF32Block, BK = kF32Block;
+  constexpr int HD = D / 2;
+  constexpr int NDB = D / 32;
+  constexpr int ROW = D * 4;
+  constexpr int OS = D + 4;
+  using VV = F32Vec<NDB>;
+  typedef typename VV::type vvec;
+  constexpr int OPND = 2 * BK * OS + NW * 2 * BQ;  // K, V rows; per wave L2, D of its tile
+  constexpr int PART = NW * BK * OS;
+  __shared__ __attribute__((aligned(16))) float smem[OPND > PART ? OPND : PART];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, l32 = lane % 32, hh = lane / 32;
+
+  // Key blocks in ascending order: when causal, the first ones see the most queries.
+  int bh, kb;
+  map_block(blockIdx.x, gridDim.x, n_kblocks, false, bh, kb);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const float *Qh = Q + head;
+  const float *Gh = dO + head;
+  const float *Dh = work + (size_t)bh * N;
+  const float *L2h = work + rows + (size_t)bh * N;
+  const int k0 = kb * BK;
+  const int krow = k0 + l32;
+
+  stage_rows_f32<D, NW>(smem, K + head, V + head, k0, N, tid);
+  __syncthreads();
+  const float *ks = smem + l32 * OS + hh * HD;
+  const float *vs = smem + (BK + l32) * OS + hh * HD;
+  float *ld = smem + 2 * BK * OS + wave * 2 * BQ;  // [L2 of the tile's queries | their D]
+
+  const int t_first = CAUSAL ? kb : 0;  // query tiles and key blocks have the same size
+  const int nt = (N + BQ - 1) / BQ;
+
+  f32x4 qf[HD / 4], gf[HD / 4];
+  vvec gg[16], qg[16];
+  auto tile_rsrc = [&](const float *base, int t) {
+    const int qa = t * BQ;
+    return make_rsrc(base + (size_t)qa * D, min(N - qa, BQ) * ROW);
+  };
+  auto load_rows = [&](f32x4 (&dst)[HD / 4], const float *base, int t) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, t);
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) dst[j] = F32Vec<4>::load(r, l32 * ROW + hh * HD * 4 + 16 * j);
+  };
+  auto load_grad = [&](vvec (&dst)[16], const float *base, int t) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, t);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[i] = VV::load(r, (8 * (i / 4) + 4 * hh + i % 4) * ROW + NDB * 4 * l32);
+  };
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  if (t_first + wave < nt) {
+    load_rows(qf, Qh, t_first + wave);
+    load_rows(gf, Gh, t_first + wave);
+  }
+  for (int t = t_first + wave; t < nt; t += NW) {
+    const int qa = t * BQ;
+    const bool more = t + NW < nt;
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) {
+      const f32x4 b = *(const f32x4 *)(ks + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(qf[j][e], b[e], s, 0, 0, 0);
+    }
+    // The fences keep each load where the registers it fills have been freed.
+    __builtin_amdgcn_sched_barrier(0);
+    load_grad(gg, Gh, t);
+    // Lane l32 + 32 hh fetches L2 (hh = 0) or D (hh = 1) of query qa + l32
+    // (zero past N); the wave shares them through its LDS slot.
+    const float lv = qa + l32 < N ? (hh ? Dh : L2h)[qa + l32] : 0.f;
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) {
+      const f32x4 b = *(const f32x4 *)(vs + 4 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dp = __builtin_amdgcn_mfma_f32_32x32x2f32(gf[j][e], b[e], dp, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_grad(qg, Qh, t);
+    __builtin_amdgcn_sched_barrier(0);
+    ld[lane] = lv;  // a wave's LDS accesses complete in order: no barrier needed
+    // Queries past N, keys past N and (causal) keys after the query give P = 0.
+    const bool edge = qa + BQ > N || k0 + BK > N || (CAUSAL && qa == k0);
+    f32x16 ds;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l2v = *(const f32x4 *)(ld + 8 * g + 4 * hh);
+      const f32x4 ddv = *(const f32x4 *)(ld + BQ + 8 * g + 4 * hh);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float p = exp2_fast(fmaf(s[r], c, -l2v[e]));
+        if (edge) {
+          const int q = qa + 8 * g + 4 * hh + e;
+          if (q >= N || krow >= N || (CAUSAL && krow > q)) p = 0.f;
+        }
+        s[r] = p;
+        ds[r] = p * (dp[r] - ddv[e]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(gg[r][db], s[r], dv[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_rows(qf, Qh, t + NW);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qg[r][db], ds[r], dk[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) load_rows(gf, Gh, t + NW);
+    // Keep the accumulators in AGPRs across iterations (else the register
+    // allocator shuttles them through VGPRs every tile).
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
+  }
+
+  __syncthreads();  // every wave is done with the K, V rows in LDS
+  merge_store_f32<D, NW>(smem, dv, wave, tid, dV + head, k0, N, 1.f);
+  __syncthreads();  // the dV partials are consumed
+  merge_store_f32<D, NW>(smem, dk, wave, tid, dK + head, k0, N, scale);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
                            const void *V, const void *O, const float *L, const void *dO, void *dQ,
@@ -447,7 +785,7 @@ hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, cons
   const int64_t rows = BH * N;
   const int ntiles = (N + kBwdRows - 1) / kBwdRows;
   constexpr int prep_rows = 256 / (D / 8);
-  hipLaunchKernelGGL((fa_bwd_prep_bf16_kernel<D>), dim3((unsigned)((rows + prep_rows - 1) / prep_rows)), dim3(256), 0, s,
+  hipLaunchKernelGGL((fa_bwd_prep_kernel<bf16, D>), dim3((unsigned)((rows + prep_rows - 1) / prep_rows)), dim3(256), 0, s,
                      (const bf16 *)O, (const bf16 *)dO, L, work, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -459,6 +797,28 @@ hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, cons
   hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(512), 0, s,
                      (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
                      (bf16 *)dK, (bf16 *)dV, N, ntiles, rows, c, scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_f32(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
+                          const void *V, const void *O, const float *L, const void *dO, void *dQ,
+                          void *dK, void *dV, float *work, float c, float scale) {
+  const int64_t rows = BH * N;
+  const int nb = (N + kF32Block - 1) / kF32Block;
+  constexpr int prep_rows = 256 / (D / 4);
+  hipLaunchKernelGGL((fa_bwd_prep_kernel<float, D>), dim3((unsigned)((rows + prep_rows - 1) / prep_rows)), dim3(256), 0, s,
+                     (const float *)O, (const float *)dO, L, work, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)(BH * nb)), dim3(64 * kF32BwdWaves), 0, s,
+                     (const float *)Q, (const float *)K, (const float *)V, (const float *)dO, work,
+                     (float *)dQ, N, nb, rows, c, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)(BH * nb)), dim3(64 * kF32BwdWaves), 0, s,
+                     (const float *)Q, (const float *)K, (const float *)V, (const float *)dO, work,
+                     (float *)dK, (float *)dV, N, nb, rows, c, scale);
   return hipGetLastError();
 }
 
@@ -479,12 +839,13 @@ extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (N > (int64_t)1 << 24) return FA_ERR_UNSUPPORTED;
-  const int64_t ntiles = (N + kBwdRows - 1) / kBwdRows;
+  const bool bf = dtype == FA_DTYPE_BF16;
+  const int64_t block_rows = bf ? kBwdRows : kF32Block;
+  const int64_t ntiles = (N + block_rows - 1) / block_rows;
   if (B * H > ((int64_t)1 << 31) / ntiles - 1) return FA_ERR_UNSUPPORTED;
   if (B * H * N > ((int64_t)1 << 31) - 256) return FA_ERR_UNSUPPORTED;  // prep grid and row indices
-  const size_t esize = 2;
+  const size_t esize = bf ? 2 : 4;
   const size_t tbytes = (size_t)B * H * N * d * esize;
   const size_t lbytes = (size_t)B * H * N * sizeof(float);
   const void *ins[] = {Q, K, V, O, dO};
@@ -510,11 +871,20 @@ extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const
   const int n = (int)N;
   const int64_t BH = B * H;
   hipError_t err;
-  if (d == 64)
-    err = causal ? launch_bwd_bf16<64, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
-                 : launch_bwd_bf16<64, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
-  else
-    err = causal ? launch_bwd_bf16<128, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
-                 : launch_bwd_bf16<128, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+  if (bf) {
+    if (d == 64)
+      err = causal ? launch_bwd_bf16<64, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
+                   : launch_bwd_bf16<64, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+    else
+      err = causal ? launch_bwd_bf16<128, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
+                   : launch_bwd_bf16<128, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+  } else {
+    if (d == 64)
+      err = causal ? launch_bwd_f32<64, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
+                   : launch_bwd_f32<64, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+    else
+      err = causal ? launch_bwd_f32<128, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
+                   : launch_bwd_f32<128, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+  }
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

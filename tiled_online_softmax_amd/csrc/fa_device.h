@@ -141,6 +141,25 @@ __device__ __forceinline__ void load_lds_share(__amdgpu_buffer_rsrc_t rsrc, uint
 #endif
 }
 
+// N_ consecutive floats at byte offset `off` of a buffer resource, one
+// range-checked load (zeros past the end).
+template <int N_>
+struct F32Vec;
+template <>
+struct F32Vec<2> {
+  typedef float type __attribute__((ext_vector_type(2)));
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(type, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+};
+template <>
+struct F32Vec<4> {
+  typedef f32x4 type;
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(type, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+};
+
 }  // namespace
 
 #endif  // FA_DEVICE_H_

@@ -384,23 +384,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
 //    bf16 kernel. In the result a lane holds 4 NDB consecutive output columns
 //    per group r/4.
 // ---------------------------------------------------------------------------
-template <int N_>
-struct F32Vec;
-template <>
-struct F32Vec<2> {
-  typedef float type __attribute__((ext_vector_type(2)));
-  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(type, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-  }
-};
-template <>
-struct F32Vec<4> {
-  typedef f32x4 type;
-  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(type, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  }
-};
-
 constexpr int kF32Rows = 32;  // query rows per workgroup (fp32 kernel)
 constexpr int kF32Keys = 32;  // keys per tile (fp32 kernel)
 
