@@ -5,13 +5,17 @@ benchmark's CPU-baseline leg may import this package. The product path (the HIP
 library and its Python binding) never imports, links or calls anything here,
 and nothing here imports the product path.
 
-Three parts:
+Four parts:
 
 * ``attention`` -- standard attention by its definition (``attention.c``):
   "Writing a FlashAttention kernel in Metal", section "Standard attention", with
   the causal rule of its section "Blockwise attention and causal masking", and L
   as defined in "FlashAttention-2 from PyTorch to Triton", section "What We Are
   Building".
+* ``attention_cross`` -- the same definition between Nq query rows and Nk key/value
+  rows, with the causal mask aligned at the top-left corner as in the kernel of
+  "FlashAttention-2 from PyTorch to Triton", section "The Triton Kernel"
+  (``attention_cross.c``).
 * ``attention_bwd`` -- the gradients of that function with respect to Q, K and V
   for a given output gradient, by the chain rule through its definition
   (``attention_bwd.c``).
@@ -19,7 +23,7 @@ Three parts:
   method itself), used by the tests to tie the recurrence to the definition.
 
 Pins: every function here is checked, in ``tests/test_oracle.py``,
-``tests/test_oracle_bwd.py`` and ``tests/test_blockwise.py``, against closed
+``tests/test_oracle_bwd.py``, ``tests/test_oracle_cross.py`` and ``tests/test_blockwise.py``, against closed
 forms, invariants, brute force on tiny inputs (central differences of the
 forward oracle for the gradients), torch's own scaled-dot-product attention in
 fp64 (and its autograd) and the worked two-block example of the first page's
@@ -37,14 +41,15 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attention.c")
 _SRC_BWD = os.path.join(_HERE, "attention_bwd.c")
+_SRC_CROSS = os.path.join(_HERE, "attention_cross.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
 def build(verbose: bool = False) -> str:
-    """Compile ``attention.c`` and ``attention_bwd.c`` into ``liboracle.so`` with gcc (no fast-math)."""
+    """Compile the oracle's C sources into ``liboracle.so`` with gcc (no fast-math)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-o", _LIB_PATH, _SRC, _SRC_BWD, "-lm"]
+           "-o", _LIB_PATH, _SRC, _SRC_BWD, _SRC_CROSS, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -53,7 +58,7 @@ def build(verbose: bool = False) -> str:
 
 def load_library(path: str):
     """Open a compiled copy of the oracle sources and declare its signatures (a copy
-    built from ``attention.c`` alone has no backward entry)."""
+    built from one source file has only that file's entry points)."""
     lib = ctypes.CDLL(path)
     lib.oracle_attention_f64.restype = ctypes.c_int
     lib.oracle_attention_f64.argtypes = [
@@ -63,6 +68,11 @@ def load_library(path: str):
     ]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    if hasattr(lib, "oracle_attention_cross_f64"):
+        lib.oracle_attention_cross_f64.restype = ctypes.c_int
+        lib.oracle_attention_cross_f64.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+            ctypes.c_int, ctypes.c_double,
+        ]
     if hasattr(lib, "oracle_attention_bwd_f64"):
         lib.oracle_attention_bwd_f64.restype = ctypes.c_int
         lib.oracle_attention_bwd_f64.argtypes = [ctypes.c_void_p] * 7 + [
@@ -76,7 +86,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
-                os.path.getmtime(_SRC), os.path.getmtime(_SRC_BWD)):
+                os.path.getmtime(_SRC), os.path.getmtime(_SRC_BWD), os.path.getmtime(_SRC_CROSS)):
             build()
         _lib = load_library(_LIB_PATH)
     return _lib
@@ -123,6 +133,40 @@ def attention(Q, K, V, causal: bool, scale: float, rows=None, lib=None):
                                   1 if causal else 0, float(scale), rows_ptr, R)
     if st != 0:
         raise RuntimeError(f"oracle_attention_f64 failed with status {st}")
+    if squeeze:
+        return O[0, 0], L[0, 0]
+    return O, L
+
+
+def attention_cross(Q, K, V, causal: bool, scale: float, lib=None):
+    """Attention between Nq query rows and Nk key/value rows in fp64.
+
+    Q: array-like [B, H, Nq, d]; K, V: [B, H, Nk, d] (or [Nq, d] / [Nk, d], treated
+    as B = H = 1), up-cast losslessly to fp64. When ``causal``, query i keeps keys
+    j <= i (mask aligned at the top-left corner).
+
+    Returns (O, L) as fp64 numpy arrays: O [B, H, Nq, d], L [B, H, Nq] (squeezed back
+    for 2-D input). ``lib`` selects another compiled copy; default: this one.
+    """
+    lib = lib or _load()
+    q = np.ascontiguousarray(np.asarray(Q, dtype=np.float64))
+    k = np.ascontiguousarray(np.asarray(K, dtype=np.float64))
+    v = np.ascontiguousarray(np.asarray(V, dtype=np.float64))
+    squeeze = q.ndim == 2
+    if squeeze:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    if (q.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2]
+            or q.shape[3] != k.shape[3]):
+        raise ValueError(f"expected [B,H,Nq,d] and two [B,H,Nk,d], got {q.shape} {k.shape} {v.shape}")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    O = np.empty((B, H, Nq, d), dtype=np.float64)
+    L = np.empty((B, H, Nq), dtype=np.float64)
+    st = lib.oracle_attention_cross_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                        O.ctypes.data, L.ctypes.data, B, H, Nq, Nk, d,
+                                        1 if causal else 0, float(scale))
+    if st != 0:
+        raise RuntimeError(f"oracle_attention_cross_f64 failed with status {st}")
     if squeeze:
         return O[0, 0], L[0, 0]
     return O, L
