@@ -28,7 +28,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, B/H/N < 1, scale not finite or <= 0, bad dtype */
-  FA_ERR_UNSUPPORTED = 2,      /* head dimension d other than 64 or 128, or a size too large */
+  FA_ERR_UNSUPPORTED = 2,      /* head dimension not supported by the entry point, or a size too large */
   FA_ERR_MISALIGNED = 3,       /* a buffer not 16-byte aligned */
   FA_ERR_LAUNCH = 4            /* the HIP runtime refused the kernel launch */
 } fa_status_t;
@@ -50,7 +50,7 @@ typedef enum {
  *            natural-log logsumexp of each row of scaled scores.
  *   B, H, N  batch, heads, sequence length (queries and keys share positions
  *            0..N-1). Each >= 1. N need not be a multiple of any tile size.
- *   d        head dimension: 64 or 128.
+ *   d        head dimension: 16, 32, 64 or 128.
  *   causal   0: every query sees every key. Non-zero: query i sees keys j <= i.
  *   scale    multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
  *   stream   hipStream_t to enqueue on (NULL = the null stream).
@@ -69,6 +69,45 @@ typedef enum {
 fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void *O, float *L,
                    int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                    void *stream, int dtype);
+
+/*
+ * fa_fwd_strided -- the forward pass of fa_fwd for the general layout of the
+ * kernel in "FlashAttention-2 from PyTorch to Triton" (section "The Triton
+ * Kernel"): separate query and key counts and arbitrary strides.
+ *
+ *   Q, O     device pointers to B x H x Nq x d arrays of `dtype`.
+ *   K, V     device pointers to B x H x Nk x d arrays of `dtype`.
+ *   L        device pointer to a B x H x Nq fp32 array; written as in fa_fwd.
+ *   x_strides  (x = q, k, v, o, l) host arrays of three element strides:
+ *            batch, head, row. The stride along d is 1. Zero batch or head
+ *            strides broadcast an input (for example one K, V head shared by
+ *            all query heads).
+ *   Nq, Nk   query rows and key rows, each >= 1 and <= 2^24.
+ *   causal   0: every query sees every key. Non-zero: query i sees keys
+ *            j <= i, positions counted from 0 in both (the mask is aligned at
+ *            the top-left corner of the Nq x Nk score matrix, as in that
+ *            page's kernel), so every query sees at least key 0.
+ *   B, H, d, scale, stream, dtype: as for fa_fwd.
+ *
+ * Requirements, checked before any device work:
+ *   - all strides >= 0 and <= 2^40; the row stride of Q, K, V and O >= d
+ *     (else FA_ERR_INVALID_ARGUMENT);
+ *   - O and L are laid out without two elements at one address, and neither
+ *     overlaps the byte range of any other operand (else
+ *     FA_ERR_INVALID_ARGUMENT);
+ *   - a row stride times the element size <= 2^24 bytes, the L row stride
+ *     < 2^31 (else FA_ERR_UNSUPPORTED);
+ *   - Q, K, V, O 16-byte aligned and their strides multiples of 16 bytes; L
+ *     4-byte aligned (else FA_ERR_MISALIGNED).
+ * Ownership, asynchrony and error behaviour as for fa_fwd. With contiguous
+ * strides and Nq = Nk = N the results equal fa_fwd's.
+ */
+fa_status_t fa_fwd_strided(const void *Q, const void *K, const void *V, void *O, float *L,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                           const int64_t *q_strides, const int64_t *k_strides,
+                           const int64_t *v_strides, const int64_t *o_strides,
+                           const int64_t *l_strides, int causal, float scale, void *stream,
+                           int dtype);
 
 /*
  * fa_bwd -- attention backward pass over B*H independent heads: the gradients
@@ -90,7 +129,8 @@ fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void *O, float *
  *   work     device workspace of 2*B*H*N floats, overwritten (per row: the
  *            sum over c of dO*O, then L * log2 e). Owned by the caller; its
  *            contents after the call carry no meaning.
- *   B,H,N,d, causal, scale, stream: as for fa_fwd.
+ *   B,H,N, causal, scale, stream: as for fa_fwd.
+ *   d        64 or 128 (16 and 32 return FA_ERR_UNSUPPORTED).
  *   dtype    FA_DTYPE_BF16 or FA_DTYPE_F32 (all of Q, K, V, O, dO and the
  *            gradients in that type).
  *

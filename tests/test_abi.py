@@ -22,7 +22,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_strided", "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -63,7 +63,7 @@ def test_bad_dtype():
     assert call(dtype=7) == fa.FA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("d", [16, 32, 63, 96, 256])
+@pytest.mark.parametrize("d", [8, 48, 63, 96, 256])
 def test_unsupported_head_dim(d):
     assert call(d=d) == fa.FA_ERR_UNSUPPORTED
 
@@ -129,3 +129,71 @@ def test_bwd_overlapping_outputs(kw):
 @pytest.mark.parametrize("name", ["Q", "dO", "dK", "work", "L"])
 def test_bwd_misaligned(name):
     assert call_bwd(**{name: BWD[name] + 4}) == fa.FA_ERR_MISALIGNED
+
+
+# fa_fwd_strided: every call below fails validation, so nothing is ever launched on
+# the fake addresses. Default: B = 1, H = 2, Nq = 64, Nk = 96, d = 64, contiguous.
+def _contig(H, N, d):
+    return (H * N * d, N * d, d)
+
+
+STR = dict(q=_contig(2, 64, 64), k=_contig(2, 96, 64), v=_contig(2, 96, 64), o=_contig(2, 64, 64),
+           l=(2 * 64, 64, 1))
+
+
+def call_strided(B=1, H=2, Nq=64, Nk=96, d=64, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16,
+                 Q=A, K=2 * A, V=3 * A, O=4 * A, L=5 * A, **st):
+    s = dict(STR, **st)
+    return fa.raw_fa_fwd_strided(Q, K, V, O, L, B, H, Nq, Nk, d, s["q"], s["k"], s["v"], s["o"], s["l"],
+                                 causal, scale, None, dtype)
+
+
+@pytest.mark.parametrize("kw", [dict(Q=0), dict(K=0), dict(V=0), dict(O=0), dict(L=0), dict(q=None),
+                                dict(k=None), dict(v=None), dict(o=None), dict(l=None)])
+def test_strided_null(kw):
+    assert call_strided(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(Nk=0), dict(B=0), dict(H=-1), dict(scale=0.0), dict(dtype=5)])
+def test_strided_bad_sizes(kw):
+    assert call_strided(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=(8192, 4096, -64)),          # negative stride
+    dict(k=(12288, 6144, 32)),          # K rows overlap (row stride < d)
+    dict(o=(8192, 32, 128)),            # O heads 32 elements apart: rows of d = 64 overlap
+    dict(o=(0, 4096, 64), B=2),         # two batches of O at one address
+    dict(l=(128, 0, 1)),                # both heads of L at one address
+    dict(O=2 * A + 64),                 # O overlaps K
+    dict(L=4 * A + 64),                 # L overlaps O
+])
+def test_strided_invalid_layouts(kw):
+    assert call_strided(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+_D256 = dict(d=256, q=_contig(2, 64, 256), k=_contig(2, 96, 256), v=_contig(2, 96, 256), o=_contig(2, 64, 256))
+
+
+_NQ = (1 << 24) + 1
+_BIG_NQ = dict(Nq=_NQ, q=_contig(2, _NQ, 64), o=_contig(2, _NQ, 64), l=(2 * _NQ, _NQ, 1))
+
+
+@pytest.mark.parametrize("kw", [dict(d=48), _D256, _BIG_NQ, dict(Nk=(1 << 24) + 1),
+                                dict(k=(1 << 26, 1 << 25, 1 << 24))])
+def test_strided_unsupported(kw):
+    assert call_strided(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(Q=A + 8), dict(V=3 * A + 4), dict(L=5 * A + 2),
+                                dict(q=(8192, 4096, 68)), dict(o=(8192 + 4, 4096, 64), B=2),
+                                dict(k=(12288, 6144, 64), v=(12288, 6148, 64))])
+def test_strided_misaligned(kw):
+    assert call_strided(**kw) == fa.FA_ERR_MISALIGNED
+
+
+def test_strided_fp32_alignment_unit():
+    # fp32 rows are 16-byte aligned at multiples of 4 elements: 68 passes the alignment
+    # check, so it is made to fail on the overlap check instead (O overlaps Q).
+    assert call_strided(dtype=fa.FA_DTYPE_F32, q=(8192 * 2, 4096 * 2, 68), O=A + 64) == fa.FA_ERR_INVALID_ARGUMENT
+    assert call_strided(dtype=fa.FA_DTYPE_F32, q=(8192, 4096, 66)) == fa.FA_ERR_MISALIGNED

@@ -1,0 +1,151 @@
+"""GPU parity of the general forward interface (fa_fwd_strided through the C ABI, and
+fa_fwd at d = 16, 32) against the fp64 oracles.
+
+Tolerances as for fa_fwd (max abs error): O 1e-5 / L 1e-4 for fp32, O 2e-2 / L 1e-2
+for bf16. Cross-attention (Nq != Nk) is compared with ``oracle.attention_cross``
+(top-left causal alignment); strided layouts are compared on contiguous copies of
+the same values.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import default_scale, make_qkv, make_qkv_cross
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 1e-2)}
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import tiled_online_softmax_amd
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return tiled_online_softmax_amd
+
+
+def _compare(O, L, Oref, Lref, dtype, label):
+    o = O.double().cpu().numpy()
+    lse = L.double().cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{label}: non-finite output"
+    eo = float(np.abs(o - Oref).max())
+    el = float(np.abs(lse - Lref).max())
+    otol, ltol = TOL[dtype]
+    print(f"[parity-strided] {label} max|dO|={eo:.3e} (tol {otol}) max|dL|={el:.3e} (tol {ltol})", flush=True)
+    assert eo <= otol and el <= ltol, f"{label}: O error {eo} (tol {otol}), L error {el} (tol {ltol})"
+
+
+def _oracle_cross(q, k, v, causal, scale):
+    return oracle.attention_cross(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
+
+
+CROSS = [(100, 300), (300, 100), (1, 257), (257, 1), (33, 65), (128, 64), (64, 200)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", CROSS)
+def test_cross_attention(fa, Nq, Nk, causal, d, dtype):
+    q, k, v = make_qkv_cross(1, 2, Nq, Nk, d, dtype, seed=Nq * 7 + Nk + d)
+    scale = default_scale(d)
+    O, L = fa.forward_strided(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    Oref, Lref = _oracle_cross(q, k, v, causal, scale)
+    _compare(O, L, Oref, Lref, dtype, f"{dtype} d={d} {Nq}x{Nk} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [16, 32])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 31, 64, 65, 200, 513])
+def test_small_head_dims(fa, N, causal, d, dtype):
+    """fa_fwd (contiguous) at d = 16 and 32, including ragged lengths."""
+    q, k, v = make_qkv(2, 2, N, d, dtype, seed=N + d)
+    scale = default_scale(d)
+    O, L = fa.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    Oref, Lref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
+    _compare(O, L, Oref, Lref, dtype, f"{dtype} d={d} N={N} causal={causal}")
+
+
+def _layouts(B, H, Nq, Nk, d, dtype, seed):
+    """(label, q, k, v) device views of the same values in several strided layouts,
+    plus the contiguous CPU tensors they hold."""
+    q, k, v = make_qkv_cross(B, H, Nq, Nk, d, dtype, seed=seed)
+    out = []
+    # [B, N, H, d] storage viewed as [B, H, N, d] (row stride H d, head stride d)
+    bshd = [t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v)]
+    out.append(("bshd", *bshd))
+    # rows padded to d + 16 elements (a slice of a wider array)
+    def padded(t):
+        w = torch.zeros(t.shape[:-1] + (d + 16,), dtype=t.dtype)
+        w[..., :d] = t
+        return w.to(DEV)[..., :d]
+    out.append(("padded_rows", *(padded(t) for t in (q, k, v))))
+    # heads of every batch stored with a gap after each head
+    def head_gap(t):
+        n = t.shape[2]
+        w = torch.zeros((t.shape[0], t.shape[1], n + 3, d), dtype=t.dtype)
+        w[:, :, :n] = t
+        return w.to(DEV)[:, :, :n]
+    out.append(("head_gap", *(head_gap(t) for t in (q, k, v))))
+    return (q, k, v), out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_strided_layouts(fa, d, causal, dtype):
+    (q, k, v), layouts = _layouts(2, 3, 150, 230, d, dtype, seed=900 + d)
+    scale = default_scale(d)
+    Oref, Lref = _oracle_cross(q, k, v, causal, scale)
+    for label, qd, kd, vd in layouts:
+        assert not (qd.is_contiguous() and kd.is_contiguous())
+        O, L = fa.forward_strided(qd, kd, vd, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        _compare(O, L, Oref, Lref, dtype, f"{label} {dtype} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_broadcast_kv_heads(fa, dtype):
+    """One K, V head shared by all 4 query heads (head stride 0) equals the oracle on
+    the repeated heads."""
+    B, H, Nq, Nk, d = 2, 4, 120, 333, 64
+    q, _, _ = make_qkv_cross(B, H, Nq, Nk, d, dtype, seed=77)
+    _, k1, v1 = make_qkv_cross(B, 1, Nq, Nk, d, dtype, seed=78)
+    scale = default_scale(d)
+    kd = k1.to(DEV).expand(B, H, Nk, d)
+    vd = v1.to(DEV).expand(B, H, Nk, d)
+    assert kd.stride(1) == 0
+    O, L = fa.forward_strided(q.to(DEV), kd, vd, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    Oref, Lref = _oracle_cross(q, k1.expand(B, H, Nk, d), v1.expand(B, H, Nk, d), True, scale)
+    _compare(O, L, Oref, Lref, dtype, f"broadcast {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_contiguous_strided_equals_fa_fwd(fa, causal, dtype):
+    """Contiguous strides and Nq = Nk: the same kernel, bitwise the same results."""
+    q, k, v = (t.to(DEV) for t in make_qkv(2, 4, 777, 128, dtype, seed=5))
+    O1, L1 = fa.forward(q, k, v, causal=causal)
+    O2, L2 = fa.forward_strided(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_strided_rejects_bad_layout(fa):
+    """A non-unit stride along d is refused by the binding; an overlapping O by the library."""
+    q, k, v = (t.to(DEV) for t in make_qkv(1, 2, 64, 64, "bf16", seed=1))
+    with pytest.raises(ValueError):
+        fa.forward_strided(q.transpose(2, 3), k, v)
+    O = torch.empty((1, 2, 64, 64), dtype=q.dtype, device=DEV)
+    L = torch.empty((1, 2, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd_strided(q, k, v, O.expand(1, 2, 64, 64)[:, :1].expand(1, 2, 64, 64), L, False, 0.125)
+    assert e.value.status == fa.FA_ERR_INVALID_ARGUMENT

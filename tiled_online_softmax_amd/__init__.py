@@ -1,7 +1,8 @@
 """Tiled online-softmax attention forward and backward passes for MI355X (gfx950).
 
-``fa_fwd`` and ``fa_bwd`` mirror the C entry points of ``libfa.so``; ``forward``
-and ``backward`` allocate the outputs (and the backward workspace) and call them.
+``fa_fwd``, ``fa_fwd_strided`` and ``fa_bwd`` mirror the C entry points of
+``libfa.so``; ``forward``, ``forward_strided`` and ``backward`` allocate the outputs
+(and the backward workspace) and call them.
 Importing fails loudly when the HIP library is not built.
 """
 
@@ -18,9 +19,12 @@ from ._binding import (  # noqa: F401
     backward,
     fa_bwd,
     fa_fwd,
+    fa_fwd_strided,
     fa_status_string,
     fa_version,
     forward,
+    forward_strided,
     raw_fa_bwd,
     raw_fa_fwd,
+    raw_fa_fwd_strided,
 )

@@ -34,6 +34,10 @@ _lib.fa_fwd.argtypes = [
     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
     ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
 ]
+_lib.fa_fwd_strided.restype = ctypes.c_int
+_lib.fa_fwd_strided.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [ctypes.c_void_p] * 5 + [
+    ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+]
 _lib.fa_bwd.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -62,6 +66,25 @@ def fa_version() -> int:
 def raw_fa_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, stream, dtype) -> int:
     """The C entry point with integer pointers; returns the status code."""
     return int(_lib.fa_fwd(Q, K, V, O, L, B, H, N, d, int(causal), float(scale), stream, int(dtype)))
+
+
+def _strides3(st):
+    """Three element strides as a C int64[3] (None passes NULL)."""
+    if st is None:
+        return None
+    st = tuple(int(x) for x in st)
+    if len(st) != 3:
+        raise ValueError("expected three strides (batch, head, row)")
+    return (ctypes.c_int64 * 3)(*st)
+
+
+def raw_fa_fwd_strided(Q, K, V, O, L, B, H, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides,
+                       l_strides, causal, scale, stream, dtype) -> int:
+    """The strided C entry point with integer pointers and stride triples; returns the status code."""
+    arrs = [_strides3(x) for x in (q_strides, k_strides, v_strides, o_strides, l_strides)]
+    ptrs = [ctypes.cast(a, ctypes.c_void_p) if a is not None else None for a in arrs]
+    return int(_lib.fa_fwd_strided(Q, K, V, O, L, B, H, Nq, Nk, d, *ptrs, int(causal), float(scale),
+                                   stream, int(dtype)))
 
 
 def raw_fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, stream, dtype) -> int:
@@ -114,6 +137,49 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, stream=No
     O = torch.empty_like(q)
     L = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, O, L, B, H, N, d, causal, scale, stream)
+    return O, L
+
+
+def fa_fwd_strided(Q, K, V, O, L, causal, scale, stream=None):
+    """Enqueue the general forward pass: Q, O [B, H, Nq, d] and K, V [B, H, Nk, d]
+    device tensors of one dtype with any strides and unit stride along d (expanded,
+    stride-0 batch or head dimensions of K and V broadcast them); L an fp32
+    [B, H, Nq] tensor. Raises FaError on a bad argument."""
+    dt = Q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    if Q.dim() != 4 or K.dim() != 4 or V.dim() != 4 or O.dim() != 4 or L.dim() != 3:
+        raise ValueError("expected 4-D Q, K, V, O and 3-D L")
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    if tuple(K.shape) != (B, H, Nk, d) or tuple(V.shape) != (B, H, Nk, d) or tuple(O.shape) != (B, H, Nq, d):
+        raise ValueError("shapes must be Q, O [B, H, Nq, d] and K, V [B, H, Nk, d]")
+    if tuple(L.shape) != (B, H, Nq) or L.dtype != torch.float32:
+        raise ValueError("L must be an fp32 [B, H, Nq] tensor")
+    for t in (Q, K, V, O):
+        if t.dtype != dt or t.stride(-1) != 1:
+            raise ValueError("Q, K, V, O must share a dtype and have unit stride along d")
+    for t in (Q, K, V, O, L):
+        if t.device.type != "cuda" or t.device != Q.device:
+            raise ValueError("all tensors must live on the same GPU")
+    st = raw_fa_fwd_strided(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, Nq, Nk, d,
+                            Q.stride()[:3], K.stride()[:3], V.stride()[:3], O.stride()[:3], L.stride(),
+                            causal, scale, _stream_handle(stream, Q.device), _DTYPES[dt])
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_strided")
+
+
+def forward_strided(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate O (with q's memory layout) and a contiguous fp32 L, run fa_fwd_strided,
+    return (O, L). q is [B, H, Nq, d]; k and v are [B, H, Nk, d]."""
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    B, H, Nq, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32).item())
+    O = torch.empty_like(q)
+    L = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_strided(q, k, v, O, L, causal, scale, stream)
     return O, L
 
 

@@ -146,6 +146,15 @@ __device__ __forceinline__ void load_lds_share(__amdgpu_buffer_rsrc_t rsrc, uint
 template <int N_>
 struct F32Vec;
 template <>
+struct F32Vec<1> {
+  typedef float type __attribute__((ext_vector_type(1)));
+  __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {
+    type v;
+    v[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    return v;
+  }
+};
+template <>
 struct F32Vec<2> {
   typedef float type __attribute__((ext_vector_type(2)));
   __device__ static type load(__amdgpu_buffer_rsrc_t r, int off) {

@@ -77,60 +77,89 @@ namespace {
 // iteration to land before the barrier that publishes it.
 // ---------------------------------------------------------------------------
 
+// One call's operands. Q, O are B x H x Nq x d, K, V are B x H x Nk x d, all
+// with unit stride along d; strides are in elements (batch, head, row). L is
+// B x H x Nq fp32 with its own strides. The host validates that every row
+// starts 16-byte aligned and that a row stride times the element size is at
+// most 2^24 bytes, so a tile of up to 64 rows spans less than 2^30 bytes (the
+// buffer-offset range used below, with 2^30 marking a load as out of range).
+struct FwdParams {
+  const void *Q, *K, *V;
+  void *O;
+  float *L;
+  int64_t q_b, q_h, k_b, k_h, v_b, v_h, o_b, o_h, l_b, l_h;
+  int q_r, k_r, v_r, o_r, l_r;
+  int H, Nq, Nk, n_qtiles;
+  float c;  // scale * log2(e)
+};
+
+// Buffer offset that always fails the range check (reads as zero).
+constexpr int kOutOfRange = 1 << 30;
+
 // Rows of a reference maximum may lag the true running maximum by up to this
 // much (base-2 exponent) before the accumulators are rescaled: weights stay
 // below 2^8, and O/l and m + log2 l do not depend on the reference chosen.
 constexpr float kRescaleSlack = 8.0f;
 
+// D < 32 (d = 16) runs on the layout of D = 32: the missing columns of the K
+// and V tiles are filled with zeros by out-of-range loads, Q's with zeros, and
+// the extra output columns are not stored.
 template <int D, bool CAUSAL, int NW, int BN>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
-    const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    bf16 *__restrict__ O, float *__restrict__ L, int N, int n_qtiles, float c) {
-  using LY = BfLayout<D, BN, NW>;
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(const FwdParams p) {
+  constexpr int DP = D < 32 ? 32 : D;    // head dimension of the tile layout
+  using LY = BfLayout<DP, BN, NW>;
   constexpr int BM = kRowsPerWave * NW;  // query rows per workgroup
   constexpr int NKB = BN / 32;           // 32-key MFMA blocks per tile
-  constexpr int NDB = D / 32;            // 32-column blocks of the output
-  constexpr int NCC = D / 16;            // 16-wide steps of the score contraction
+  constexpr int NDB = DP / 32;           // 32-column blocks of the output
+  constexpr int NCC = DP / 16;           // 16-wide steps of the score contraction
   __shared__ __attribute__((aligned(1024))) char smem[2 * LY::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: keep it in an SGPR
   const int lane = tid % 64;
   const int l32 = lane % 32, hh = lane / 32;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const float c = p.c;
 
   int bh, qt;
-  map_block(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, bh, qt);
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const bf16 *Qh = Q + head;
-  const bf16 *Kh = K + head;
-  const bf16 *Vh = V + head;
+  map_block(blockIdx.x, gridDim.x, p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H, h = bh - b * p.H;
+  const bf16 *Qh = (const bf16 *)p.Q + b * p.q_b + h * p.q_h;
+  const bf16 *Kh = (const bf16 *)p.K + b * p.k_b + h * p.k_h;
+  const bf16 *Vh = (const bf16 *)p.V + b * p.v_b + h * p.v_h;
 
   const int q0 = qt * BM;
   const int qw = q0 + kRowsPerWave * wave;  // first query row of this wave
   const int qrow = qw + l32;                // the query row this lane carries
-  const bool wave_live = qw < N;            // wave has rows to compute (uniform)
+  const bool wave_live = qw < Nq;           // wave has rows to compute (uniform)
 
   // Per-lane byte offsets (within a tile) of this wave's share of the tile loads:
   // LDS slot p = 1024 * gi + 16 * lane holds chunk (slot ^ swz(row)) of row p / ROW.
   // Load i adds 1024 i through its instruction offset, so it is taken out here.
+  // Chunks past the D columns of a row (d = 16) read out of range: zeros.
+  const int krs = 2 * p.k_r, vrs = 2 * p.v_r;  // row strides in bytes
   int kvo[LY::LPW], vvo[LY::LPW];
 #pragma unroll
   for (int i = 0; i < LY::LPW; ++i) {
-    const int p = 64 * (wave * LY::LPW + i) + lane;  // 16-byte slot index in the tile
-    const int r = p / LY::CPR, j = p % LY::CPR;
-    kvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_k(r)) - 1024 * i;
-    vvo[i] = r * LY::ROW + 16 * (j ^ LY::swz_v(r)) - 1024 * i;
+    const int sl = 64 * (wave * LY::LPW + i) + lane;  // 16-byte slot index in the tile
+    const int r = sl / LY::CPR, j = sl % LY::CPR;
+    const int jk = j ^ LY::swz_k(r), jv = j ^ LY::swz_v(r);
+    kvo[i] = (16 * jk < 2 * D ? r * krs + 16 * jk : kOutOfRange) - 1024 * i;
+    vvo[i] = (16 * jv < 2 * D ? r * vrs + 16 * jv : kOutOfRange) - 1024 * i;
   }
   const uint32_t smem_lds = lds_addr(smem);
+  // Range of a tile: its last row ends the buffer, so rows past Nk read as zero.
   auto issue_k = [&](int t) {
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Kh + (size_t)k0 * D, min(N - k0, BN) * LY::ROW);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(Kh + (size_t)k0 * p.k_r, (min(Nk - k0, BN) - 1) * krs + 2 * D);
     const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + 1024 * wave * LY::LPW;
     load_lds_share(rs, dst, kvo);
   };
   auto issue_v = [&](int t) {
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(Vh + (size_t)k0 * D, min(N - k0, BN) * LY::ROW);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(Vh + (size_t)k0 * p.v_r, (min(Nk - k0, BN) - 1) * vrs + 2 * D);
     const uint32_t dst = smem_lds + (t & 1) * LY::STAGE + LY::TILE + 1024 * wave * LY::LPW;
     load_lds_share(rs, dst, vvo);
   };
@@ -145,12 +174,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   const int vchunk = 2 * ((lane / 16) % 2) + (lane % 4) / 2;  // chunk within a 32-column block
   const int vbase = vrow * LY::ROW + 16 * (vchunk ^ LY::swz_v(vrow)) + 8 * (lane % 2);
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16cc + 8hh + 0..7].
+  // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16cc + 8hh + 0..7]
+  // (zeros past row Nq or column D).
   bf16x8 qf[NCC];
 #pragma unroll
   for (int cc = 0; cc < NCC; ++cc) {
-    if (qrow < N)
-      qf[cc] = *(const bf16x8 *)(Qh + (size_t)qrow * D + 16 * cc + 8 * hh);
+    if (qrow < Nq && 16 * cc + 8 * hh < D)
+      qf[cc] = *(const bf16x8 *)(Qh + (size_t)qrow * p.q_r + 16 * cc + 8 * hh);
     else
       qf[cc] = bf16x8{};
   }
@@ -161,15 +191,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   float m = -INFINITY;  // reference row maximum (base-2 scaled domain)
   float lsum = 0.f;     // row sum relative to m over this half-wave's keys
 
-  const int kend = CAUSAL ? min(N, q0 + BM) : N;
+  const int kend = CAUSAL ? min(Nk, q0 + BM) : Nk;
   const int nt = (kend + BN - 1) / BN;
   // Leading tiles that need no mask for any row of the workgroup.
-  const int nfull = CAUSAL ? min((q0 + 1) / BN, N / BN) : N / BN;
+  const int nfull = CAUSAL ? min((q0 + 1) / BN, Nk / BN) : Nk / BN;
 
   // Is 32-key block kb of tile t needed by this wave? (always, off the edge)
   auto block_live = [&](int t, int kb) {
     const int kb0 = t * BN + 32 * kb;
-    return kb0 < N && (!CAUSAL || kb0 <= qw + kRowsPerWave - 1);
+    return kb0 < Nk && (!CAUSAL || kb0 <= qw + kRowsPerWave - 1);
   };
 
   // S^T blocks of 32 keys x 32 queries for tile t. Result layout: lane (l32, hh),
@@ -198,7 +228,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb0 + 8 * (r / 4) + 4 * hh + (r % 4);
-        const bool bad = key >= N || (CAUSAL && key > qrow);
+        const bool bad = key >= Nk || (CAUSAL && key > qrow);
         s[kb][r] = bad ? -INFINITY : s[kb][r];
       }
     }
@@ -318,7 +348,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   issue_v(0);
   if (nt > 1) issue_k(1);
   publish();
-  // Waves whose rows all lie past N (only in the last query tile of a ragged
+  // Waves whose rows all lie past Nq (only in the last query tile of a ragged
   // sequence) run the same code on zero Q rows and store nothing: no branch
   // around the loop, so the Q loads are known complete before it.
   // Tile 0 is computed for every block (the mask removes dead ones), so every
@@ -342,19 +372,20 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(
   if (!wave_live) return;
   // Epilogue: one division by the row sum (both half-waves' keys), RNE to bf16.
   const float ltot = halves_sum(lsum);
-  if (qrow < N) {
+  if (qrow < Nq) {
     const float inv = 1.f / ltot;
-    bf16 *orow = O + head + (size_t)qrow * D;
+    bf16 *orow = (bf16 *)p.O + b * p.o_b + h * p.o_h + (size_t)qrow * p.o_r;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        if (D < DP && 8 * g + 4 * hh >= D) continue;  // padding columns (d = 16)
         bf16x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v4[e] = (bf16)(o[db][4 * g + e] * inv);
         *(bf16x4 *)(orow + 32 * db + 8 * g + 4 * hh) = v4;
       }
-    if (hh == 0) L[(size_t)bh * N + qrow] = (m + log2_fast(ltot)) * kLn2;
+    if (hh == 0) p.L[b * p.l_b + h * p.l_h + (size_t)qrow * p.l_r] = (m + log2_fast(ltot)) * kLn2;
   }
 }
 
@@ -389,15 +420,16 @@ constexpr int kF32Keys = 32;  // keys per tile (fp32 kernel)
 
 // Two workgroups of four waves per CU at d = 64 (at most 256 VGPRs a wave, so
 // the MFMA accumulators stay in VGPRs and are rescaled in place).
+//
+// D = 16 keeps the 32-row output blocks: lanes l32 >= 16 read V columns past
+// the row (or zeros past the tile) into output rows that are never stored.
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 2 : 1) void fa_fwd_f32_kernel(
-    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
-    float *__restrict__ O, float *__restrict__ L, int N, int n_qblocks, float c) {
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 2 : 1) void fa_fwd_f32_kernel(const FwdParams p) {
   constexpr int BN = kF32Keys;
-  constexpr int HD = D / 2;    // contraction steps of S^T per tile
-  constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  constexpr int ROW = D * 4;   // bytes per row
-  constexpr int OS = D + 4;    // row stride (floats) of the merge buffer
+  constexpr int DP = D < 32 ? 32 : D;  // columns of the output blocks
+  constexpr int HD = D / 2;            // contraction steps of S^T per tile
+  constexpr int NDB = DP / 32;         // 32-row blocks of O^T
+  constexpr int OS = DP + 4;           // row stride (floats) of the merge buffer
   using VV = F32Vec<NDB>;
   typedef typename VV::type vvec;
 
@@ -407,44 +439,48 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 2 : 1) void fa_fwd_
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, l32 = lane % 32, hh = lane / 32;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const float c = p.c;
 
   int bh, qb;
-  map_block(blockIdx.x, gridDim.x, n_qblocks, CAUSAL, bh, qb);
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const float *Kh = K + head;
-  const float *Vh = V + head;
+  map_block(blockIdx.x, gridDim.x, p.n_qtiles, CAUSAL, bh, qb);
+  const int b = bh / p.H, h = bh - b * p.H;
+  const float *Kh = (const float *)p.K + b * p.k_b + h * p.k_h;
+  const float *Vh = (const float *)p.V + b * p.v_b + h * p.v_h;
+  const int qrs = 4 * p.q_r, krs = 4 * p.k_r, vrs = 4 * p.v_r;  // row strides in bytes
   const int q0 = qb * kF32Rows;
   const int qrow = q0 + l32;
 
-  // Q rows of the block (rows past N read as zero).
+  // Q rows of the block (rows past Nq read as zero; the range ends with the last row).
   float qf[HD];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head + (size_t)q0 * D, min(N - q0, kF32Rows) * ROW);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const float *)p.Q + b * p.q_b + h * p.q_h + (size_t)q0 * p.q_r,
+                                                (min(Nq - q0, kF32Rows) - 1) * qrs + 4 * D);
 #pragma unroll
     for (int j = 0; j < HD / 4; ++j) {
-      const f32x4 w = F32Vec<4>::load(rq, l32 * ROW + hh * HD * 4 + 16 * j);
+      const f32x4 w = F32Vec<4>::load(rq, l32 * qrs + hh * HD * 4 + 16 * j);
 #pragma unroll
       for (int e = 0; e < 4; ++e) qf[4 * j + e] = w[e];
     }
   }
 
-  const int kend = CAUSAL ? min(N, q0 + kF32Rows) : N;
+  const int kend = CAUSAL ? min(Nk, q0 + kF32Rows) : Nk;
   const int nt = (kend + BN - 1) / BN;
 
   f32x4 kf[HD / 4];  // K operand of one tile
   vvec vf[16];       // V operands of one tile, one vector per MFMA step
   auto load_k = [&](int t) {
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)k0 * D, min(N - k0, BN) * ROW);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)k0 * p.k_r, (min(Nk - k0, BN) - 1) * krs + 4 * D);
 #pragma unroll
-    for (int j = 0; j < HD / 4; ++j) kf[j] = F32Vec<4>::load(rk, l32 * ROW + hh * HD * 4 + 16 * j);
+    for (int j = 0; j < HD / 4; ++j) kf[j] = F32Vec<4>::load(rk, l32 * krs + hh * HD * 4 + 16 * j);
   };
   auto load_v = [&](int t) {
     const int k0 = t * BN;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)k0 * D, min(N - k0, BN) * ROW);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)k0 * p.v_r, (min(Nk - k0, BN) - 1) * vrs + 4 * D);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      vf[r] = VV::load(rv, (8 * (r / 4) + 4 * hh + r % 4) * ROW + NDB * 4 * l32);
+      vf[r] = VV::load(rv, (8 * (r / 4) + 4 * hh + r % 4) * vrs + NDB * 4 * l32);
   };
 
   f32x16 o[NDB];
@@ -467,11 +503,11 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 2 : 1) void fa_fwd_
     if (more) load_k(t + NW);
 
     // Ragged end and the causal diagonal tile (k0 == q0) only.
-    if (k0 + BN > N || (CAUSAL && k0 + BN > q0)) {
+    if (k0 + BN > Nk || (CAUSAL && k0 + BN > q0)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 8 * (r / 4) + 4 * hh + r % 4;
-        if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+        if (key >= Nk || (CAUSAL && key > qrow)) s[r] = -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -532,14 +568,16 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 2 : 1) void fa_fwd_
       }
   }
   __syncthreads();
-  // Sum the partial outputs, divide once by the merged row sum, store.
+  // Sum the partial outputs, divide once by the merged row sum, store the D
+  // columns.
   constexpr int C4 = D / 4;
-  static_assert(kF32Rows * C4 % (NW * 64) == 0, "merge must split evenly over the workgroup");
+  float *Ob = (float *)p.O + b * p.o_b + h * p.o_h;
+  float *Lb = p.L + b * p.l_b + h * p.l_h;
 #pragma unroll
-  for (int it = 0; it < kF32Rows * C4 / (NW * 64); ++it) {
+  for (int it = 0; it < (kF32Rows * C4 + NW * 64 - 1) / (NW * 64); ++it) {
     const int idx = tid + NW * 64 * it;
     const int row = idx / C4, c4 = idx % C4;
-    if (q0 + row >= N) continue;
+    if (row >= kF32Rows || q0 + row >= Nq) continue;
     float mrow = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mrow = fmaxf(mrow, Ms[w][row]);
@@ -551,16 +589,14 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 && D == 64) ? 2 : 1) void fa_fwd_
       acc += *(const f32x4 *)(&Os[w][row * OS + 4 * c4]);
     }
     const float inv = 1.f / lrow;
-    *(f32x4 *)(O + head + (size_t)(q0 + row) * D + 4 * c4) = acc * inv;
-    if (c4 == 0) L[(size_t)bh * N + q0 + row] = (mrow + log2_fast(lrow)) * kLn2;
+    *(f32x4 *)(Ob + (size_t)(q0 + row) * p.o_r + 4 * c4) = acc * inv;
+    if (c4 == 0) Lb[(size_t)(q0 + row) * p.l_r] = (mrow + log2_fast(lrow)) * kLn2;
   }
 }
 
-hipError_t launch(const void *kern, int nblocks, int threads, hipStream_t stream, const void *Q,
-                  const void *K, const void *V, void *O, float *L, int N, int n_qtiles, float c) {
-  void *args[] = {(void *)&Q, (void *)&K, (void *)&V, (void *)&O,
-                  (void *)&L, (void *)&N, (void *)&n_qtiles, (void *)&c};
-  return hipLaunchKernel(kern, dim3(nblocks), dim3(threads), args, 0, stream);
+hipError_t launch(const void *kern, int64_t nblocks, int threads, hipStream_t stream, FwdParams p) {
+  void *args[] = {(void *)&p};
+  return hipLaunchKernel(kern, dim3((unsigned)nblocks), dim3(threads), args, 0, stream);
 }
 
 // Tile configuration of the bf16 kernel: waves per workgroup (32 query rows
@@ -574,14 +610,13 @@ hipError_t launch(const void *kern, int nblocks, int threads, hipStream_t stream
 constexpr int kBf16Waves = FA_BF16_NW;
 constexpr int kBf16Keys = FA_BF16_BN;
 
+constexpr int kBf16Rows = kRowsPerWave * kBf16Waves;  // query rows per workgroup
+
 template <int D, bool CAUSAL>
-hipError_t launch_bf16(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
-                       const void *V, void *O, float *L, float c) {
-  constexpr int BM = kRowsPerWave * kBf16Waves;
-  const int nq = (N + BM - 1) / BM;
+hipError_t launch_bf16(int64_t BH, hipStream_t s, FwdParams p) {
+  p.n_qtiles = (p.Nq + kBf16Rows - 1) / kBf16Rows;
   const void *kern = (const void *)&fa_fwd_bf16_kernel<D, CAUSAL, kBf16Waves, kBf16Keys>;
-  return launch(kern, (int)(BH * nq),
-                64 * kBf16Waves, s, Q, K, V, O, L, N, nq, c);
+  return launch(kern, BH * p.n_qtiles, 64 * kBf16Waves, s, p);
 }
 
 // Waves per workgroup of the fp32 kernel (each takes every NW-th key tile).
@@ -591,17 +626,87 @@ hipError_t launch_bf16(int64_t BH, int N, hipStream_t s, const void *Q, const vo
 constexpr int kF32Waves = FA_F32_NW;
 
 template <int D, bool CAUSAL>
-hipError_t launch_f32(int64_t BH, int N, hipStream_t s, const void *Q, const void *K,
-                      const void *V, void *O, float *L, float c) {
-  const int nq = (N + kF32Rows - 1) / kF32Rows;
+hipError_t launch_f32(int64_t BH, hipStream_t s, FwdParams p) {
+  p.n_qtiles = (p.Nq + kF32Rows - 1) / kF32Rows;
   const void *kern = (const void *)&fa_fwd_f32_kernel<D, CAUSAL, kF32Waves>;
-  return launch(kern, (int)(BH * nq), 64 * kF32Waves, s, Q, K, V, O, L, N, nq, c);
+  return launch(kern, BH * p.n_qtiles, 64 * kF32Waves, s, p);
+}
+
+// Enqueue the kernel for (dtype, d, causal); the arguments are validated.
+hipError_t dispatch(int dtype, int64_t d, bool causal, int64_t BH, hipStream_t s, const FwdParams &p) {
+#define FA_CASE(DD)                                                                              \
+  case DD:                                                                                       \
+    if (dtype == FA_DTYPE_BF16)                                                                  \
+      return causal ? launch_bf16<DD, true>(BH, s, p) : launch_bf16<DD, false>(BH, s, p);        \
+    return causal ? launch_f32<DD, true>(BH, s, p) : launch_f32<DD, false>(BH, s, p);
+  switch (d) {
+    FA_CASE(16)
+    FA_CASE(32)
+    FA_CASE(64)
+    FA_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef FA_CASE
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
 }
+
+
+bool supported_head_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Row counts up to 2^24 keep every row index in 32 bits; the grid stays below 2^31.
+bool supported_sizes(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk) {
+  if (Nq > (int64_t)1 << 24 || Nk > (int64_t)1 << 24) return false;
+  const int64_t block_rows = dtype == FA_DTYPE_BF16 ? kBf16Rows : kF32Rows;
+  const int64_t n_qtiles = (Nq + block_rows - 1) / block_rows;
+  return B * H <= ((int64_t)1 << 31) / n_qtiles - 1;
+}
+
+// Byte range [lo, hi) covered by a B x H x rows x inner array with element
+// strides st (batch, head, row) and unit stride inside a row.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span tensor_span(const void *base, int64_t B, int64_t H, int64_t rows, int64_t inner, const int64_t st[3],
+                 size_t esize) {
+  const int64_t last = (B - 1) * st[0] + (H - 1) * st[1] + (rows - 1) * st[2] + inner;
+  return {(uintptr_t)base, (uintptr_t)base + (uintptr_t)last * esize};
+}
+bool spans_overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// No two elements share an address: taken in increasing stride order, every
+// dimension of extent > 1 steps over the whole span of the ones inside it.
+bool non_overlapping(int64_t B, int64_t H, int64_t rows, int64_t inner, const int64_t st[3]) {
+  int64_t ext[3] = {B, H, rows}, str[3] = {st[0], st[1], st[2]};
+  for (int i = 0; i < 3; ++i)  // sort the three dimensions by stride
+    for (int j = i + 1; j < 3; ++j)
+      if (str[j] < str[i]) {
+        int64_t t = str[i];
+        str[i] = str[j];
+        str[j] = t;
+        t = ext[i];
+        ext[i] = ext[j];
+        ext[j] = t;
+      }
+  int64_t span = inner;
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] == 1) continue;
+    if (str[i] < span) return false;
+    span += (ext[i] - 1) * str[i];
+  }
+  return true;
+}
+
+fa_status_t launch_checked(int dtype, int64_t d, int causal, int64_t BH, void *stream, const FwdParams &p) {
+  const hipError_t err = dispatch(dtype, d, causal != 0, BH, (hipStream_t)stream, p);
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+float log2e_scale(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
 }  // namespace
 
@@ -613,12 +718,8 @@ extern "C" fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void 
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
   const size_t esize = dtype == FA_DTYPE_BF16 ? 2 : 4;
-  // Sizes: 32-bit row indices inside a head, grid size below 2^31.
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (N > (int64_t)1 << 24) return FA_ERR_UNSUPPORTED;
-  const int64_t block_rows = dtype == FA_DTYPE_BF16 ? kRowsPerWave * kBf16Waves : kF32Rows;
-  const int64_t n_qtiles = (N + block_rows - 1) / block_rows;
-  if (B * H > ((int64_t)1 << 31) / n_qtiles - 1) return FA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(d)) return FA_ERR_UNSUPPORTED;
+  if (!supported_sizes(dtype, B, H, N, N)) return FA_ERR_UNSUPPORTED;
   const size_t nelem = (size_t)B * (size_t)H * (size_t)N * (size_t)d;
   const size_t obytes = nelem * esize, lbytes = (size_t)B * H * N * sizeof(float);
   if (overlaps(O, obytes, Q, obytes) || overlaps(O, obytes, K, obytes) ||
@@ -629,27 +730,91 @@ extern "C" fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void 
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)L) & 15)
     return FA_ERR_MISALIGNED;
 
-  const float c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
-  hipStream_t s = (hipStream_t)stream;
-  const int n = (int)N;
-  const int64_t BH = B * H;
-  hipError_t err;
-  if (dtype == FA_DTYPE_BF16) {
-    if (d == 64)
-      err = causal ? launch_bf16<64, true>(BH, n, s, Q, K, V, O, L, c)
-                   : launch_bf16<64, false>(BH, n, s, Q, K, V, O, L, c);
-    else
-      err = causal ? launch_bf16<128, true>(BH, n, s, Q, K, V, O, L, c)
-                   : launch_bf16<128, false>(BH, n, s, Q, K, V, O, L, c);
-  } else {
-    if (d == 64)
-      err = causal ? launch_f32<64, true>(BH, n, s, Q, K, V, O, L, c)
-                   : launch_f32<64, false>(BH, n, s, Q, K, V, O, L, c);
-    else
-      err = causal ? launch_f32<128, true>(BH, n, s, Q, K, V, O, L, c)
-                   : launch_f32<128, false>(BH, n, s, Q, K, V, O, L, c);
-  }
-  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  FwdParams p{};
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.L = L;
+  p.q_h = p.k_h = p.v_h = p.o_h = N * d;
+  p.q_b = p.k_b = p.v_b = p.o_b = H * N * d;
+  p.q_r = p.k_r = p.v_r = p.o_r = (int)d;
+  p.l_b = H * N;
+  p.l_h = N;
+  p.l_r = 1;
+  p.H = (int)H;
+  p.Nq = p.Nk = (int)N;
+  p.c = log2e_scale(scale);
+  return launch_checked(dtype, d, causal, B * H, stream, p);
+}
+
+extern "C" fa_status_t fa_fwd_strided(const void *Q, const void *K, const void *V, void *O, float *L,
+                                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                      const int64_t *q_strides, const int64_t *k_strides,
+                                      const int64_t *v_strides, const int64_t *o_strides,
+                                      const int64_t *l_strides, int causal, float scale, void *stream,
+                                      int dtype) {
+  if (!Q || !K || !V || !O || !L || !q_strides || !k_strides || !v_strides || !o_strides || !l_strides)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
+  const int64_t *ts[4] = {q_strides, k_strides, v_strides, o_strides};
+  for (const int64_t *st : ts)
+    for (int i = 0; i < 3; ++i)
+      if (st[i] < 0 || st[i] > ((int64_t)1 << 40)) return FA_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 3; ++i)
+    if (l_strides[i] < 0 || l_strides[i] > ((int64_t)1 << 40)) return FA_ERR_INVALID_ARGUMENT;
+  for (const int64_t *st : ts)
+    if (st[2] < d) return FA_ERR_INVALID_ARGUMENT;  // rows of a tensor do not overlap
+  if (!non_overlapping(B, H, Nq, d, o_strides) || !non_overlapping(B, H, Nq, 1, l_strides))
+    return FA_ERR_INVALID_ARGUMENT;
+  const size_t esize = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  if (!supported_head_dim(d)) return FA_ERR_UNSUPPORTED;
+  if (!supported_sizes(dtype, B, H, Nq, Nk)) return FA_ERR_UNSUPPORTED;
+  for (const int64_t *st : ts)
+    if (st[2] * (int64_t)esize > ((int64_t)1 << 24)) return FA_ERR_UNSUPPORTED;
+  if (l_strides[2] > ((int64_t)1 << 31) - 1) return FA_ERR_UNSUPPORTED;
+  const Span sq = tensor_span(Q, B, H, Nq, d, q_strides, esize);
+  const Span sk = tensor_span(K, B, H, Nk, d, k_strides, esize);
+  const Span sv = tensor_span(V, B, H, Nk, d, v_strides, esize);
+  const Span so = tensor_span(O, B, H, Nq, d, o_strides, esize);
+  const Span sl = tensor_span(L, B, H, Nq, 1, l_strides, sizeof(float));
+  if (spans_overlap(so, sq) || spans_overlap(so, sk) || spans_overlap(so, sv) || spans_overlap(so, sl) ||
+      spans_overlap(sl, sq) || spans_overlap(sl, sk) || spans_overlap(sl, sv))
+    return FA_ERR_INVALID_ARGUMENT;
+  const int64_t emask = 16 / (int64_t)esize - 1;  // element strides keep 16-byte row alignment
+  if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15) return FA_ERR_MISALIGNED;
+  if ((uintptr_t)L & 3) return FA_ERR_MISALIGNED;
+  for (const int64_t *st : ts)
+    if ((st[0] | st[1] | st[2]) & emask) return FA_ERR_MISALIGNED;
+
+  FwdParams p{};
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.L = L;
+  p.q_b = q_strides[0];
+  p.q_h = q_strides[1];
+  p.q_r = (int)q_strides[2];
+  p.k_b = k_strides[0];
+  p.k_h = k_strides[1];
+  p.k_r = (int)k_strides[2];
+  p.v_b = v_strides[0];
+  p.v_h = v_strides[1];
+  p.v_r = (int)v_strides[2];
+  p.o_b = o_strides[0];
+  p.o_h = o_strides[1];
+  p.o_r = (int)o_strides[2];
+  p.l_b = l_strides[0];
+  p.l_h = l_strides[1];
+  p.l_r = (int)l_strides[2];
+  p.H = (int)H;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.c = log2e_scale(scale);
+  return launch_checked(dtype, d, causal, B * H, stream, p);
 }
 
 extern "C" const char *fa_status_string(int status) {

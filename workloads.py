@@ -109,6 +109,19 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     return q.to(t).contiguous(), k.to(t).contiguous(), v.to(t).contiguous()
 
 
+def make_qkv_cross(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int,
+                   sigma_qk: float = 1.0, sigma_v: float = 1.0):
+    """Q [B, H, Nq, d] and K, V [B, H, Nk, d] on the CPU, contiguous, in the given element
+    type: Q, then K, then V drawn as N(0, 1) fp32 and scaled, as in ``make_qkv``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32) * sigma_qk
+    k = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * sigma_qk
+    v = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * sigma_v
+    t = torch_dtype(dtype)
+    return q.to(t).contiguous(), k.to(t).contiguous(), v.to(t).contiguous()
+
+
 def sample_rows(N: int, count: int, seed: int):
     """Sorted distinct query rows for sampled checks: first, last, and seeded others."""
     g = torch.Generator(device="cpu")
