@@ -38,7 +38,8 @@ METRIC_BWD = "attn bwd TFLOP/s & % MFMA peak (bf16, causal, B4 H16 N4096 d128)"
 def metric_name(which: str, w) -> str:
     """The metric string for a pass and workload (METRIC / METRIC_BWD for the default one)."""
     mask = "causal" if w.causal else "non-causal"
-    return f"attn {which} TFLOP/s & % MFMA peak ({w.dtype}, {mask}, B{w.B} H{w.H} N{w.N} d{w.d})"
+    n = f"Nq{w.N} Nk{w.keys}" if w.keys != w.N else f"N{w.N}"
+    return f"attn {which} TFLOP/s & % MFMA peak ({w.dtype}, {mask}, B{w.B} H{w.H} {n} d{w.d})"
 # MI355X published dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU;
 # fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
@@ -103,6 +104,42 @@ def cpu_baseline(w, q, k, v, O, L, target_s: float):
     }
 
 
+def cpu_baseline_cross(w, q, k, v, O, L, target_s: float):
+    """Time the cross-attention oracle on whole heads, one after another, until about
+    half the target time has passed; check those heads."""
+    import numpy as np
+
+    import oracle
+
+    o = O.double().cpu().numpy()
+    l = L.double().cpu().numpy()
+    t, heads, eo, el = 0.0, 0, 0.0, 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            args = [x[sl].double().numpy() for x in (q, k, v)]
+            t0 = time.perf_counter()
+            Oref, Lref = oracle.attention_cross(*args, w.causal, w.scale)
+            t += time.perf_counter() - t0
+            heads += 1
+            eo = max(eo, float(np.max(np.abs(o[sl] - Oref))))
+            el = max(el, float(np.max(np.abs(l[sl] - Lref))))
+            if t >= 0.5 * target_s:
+                break
+        if t >= 0.5 * target_s:
+            break
+    flops = 4.0 * w.d * float(w.pairs()) * heads
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{heads} whole heads of {w.B * w.H} (full Nq x Nk S and P in fp64), {t:.1f} s",
+        "seconds": t,
+        "sampled_heads_max_abs_err": {"O": eo, "L": el},
+    }
+
+
 def cpu_baseline_bwd(w, q, k, v, do, dQ, dK, dV):
     """Time the backward oracle on the first head (all rows: dK and dV need every
     query); check that head of the GPU gradients against it."""
@@ -160,6 +197,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward pass")
+    ap.add_argument("--layout", choices=("contiguous", "bshd"), default="contiguous",
+                    help="forward only: bshd stores Q, K, V, O as [B, N, H, d] and calls fa_fwd_strided")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run three plain device copies of MIB MiB each "
                          "(reference dispatches for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -180,9 +219,17 @@ def main():
     from workloads import HEADLINE, WORKLOADS
 
     w = WORKLOADS[args.workload or HEADLINE]
+    strided = args.layout == "bshd" or w.keys != w.N
+    if args.which == "bwd" and strided:
+        print("the backward pass takes contiguous [B, H, N, d] tensors with Nq = Nk", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     q, k, v = w.make()
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    if args.layout == "bshd":
+        # [B, N, H, d] storage, viewed as [B, H, N, d]
+        qd, kd, vd = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2) for t in (q, k, v))
+    else:
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     O = torch.empty_like(qd)
     L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -197,6 +244,9 @@ def main():
 
         def step():
             fa.fa_bwd(qd, kd, vd, O, L, dod, dQ, dK, dV, work, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+    elif strided:
+        def step():
+            fa.fa_fwd_strided(qd, kd, vd, O, L, w.causal, w.scale, stream)
     else:
         def step():
             fa.fa_fwd(qd, kd, vd, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
@@ -230,7 +280,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = None if bwd else measured_traffic(w.name)
+    traffic = None if (bwd or strided) else measured_traffic(w.name)
     # backward: Q, K, V, O, dO read and dQ, dK, dV written once, plus L
     n_rows = w.B * w.H * w.N
     io_bytes = (2 * (w.io_bytes() - 4 * n_rows) + 4 * n_rows) if bwd else w.io_bytes()
@@ -268,9 +318,17 @@ def main():
     }
     if bwd:
         rec["roofline"]["kernel_ms"]["covers"] = "one fa_bwd call: preprocessing, dQ and dK/dV kernels"
+    if strided:
+        rec["config"]["Nk"] = w.keys
+        rec["config"]["layout"] = args.layout
+        rec["roofline"]["kernel_ms"]["covers"] = "one fa_fwd_strided call"
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = (cpu_baseline_bwd(w, q, k, v, do, dQ, dK, dV) if bwd
-                               else cpu_baseline(w, q, k, v, O, L, args.cpu_seconds))
+        if bwd:
+            rec["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, dQ, dK, dV)
+        elif w.keys != w.N:
+            rec["cpu_baseline"] = cpu_baseline_cross(w, q, k, v, O, L, args.cpu_seconds)
+        else:
+            rec["cpu_baseline"] = cpu_baseline(w, q, k, v, O, L, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 

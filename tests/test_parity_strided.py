@@ -149,3 +149,23 @@ def test_strided_rejects_bad_layout(fa):
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd_strided(q, k, v, O.expand(1, 2, 64, 64)[:, :1].expand(1, 2, 64, 64), L, False, 0.125)
     assert e.value.status == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "bshd"])
+def test_cross_workload_full_size(fa, layout):
+    """The benchmarked cross-attention workload at full size (B=4, H=16, 1024 queries,
+    4096 keys, d=128), in the launch the benchmark times; two heads against the oracle."""
+    from workloads import WORKLOADS
+
+    w = WORKLOADS["cross_bf16_b4h16q1024k4096d128"]
+    q, k, v = w.make()
+    if layout == "bshd":
+        qd, kd, vd = (t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v))
+    else:
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    O, L = fa.forward_strided(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 0), (3, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        Oref, Lref = _oracle_cross(q[sl], k[sl], v[sl], w.causal, w.scale)
+        _compare(O[sl], L[sl], Oref, Lref, "bf16", f"cross workload {layout} head ({b},{h})")

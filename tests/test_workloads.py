@@ -40,3 +40,21 @@ def test_workload_table():
     assert default_scale(128) == torch.tensor(1 / math.sqrt(128), dtype=torch.float32).item()
     r = sample_rows(1000, 16, seed=5)
     assert r[0] == 0 and r[-1] == 999 and len(r) == 16 and len(set(r)) == 16
+
+
+def test_pairs_counts_admitted_keys():
+    """pairs() equals a direct count of (query, key) pairs admitted by the top-left rule."""
+    from workloads import Workload
+
+    for (n, nk) in ((5, 5), (5, 9), (9, 5), (1, 7), (7, 1)):
+        for causal in (False, True):
+            w = Workload("t", 1, 1, n, 16, "f32", causal, seed=0, Nk=nk if nk != n else 0)
+            count = sum(1 for i in range(n) for j in range(nk) if not causal or j <= i)
+            assert w.pairs() == count, (n, nk, causal)
+
+
+def test_cross_workload_shapes():
+    w = WORKLOADS["cross_bf16_b4h16q1024k4096d128"]
+    q, k, v = w.make()
+    assert q.shape == (4, 16, 1024, 128) and k.shape == v.shape == (4, 16, 4096, 128)
+    assert w.io_bytes() == 2 * (4 * 16 * (1024 + 4096)) * 128 * 2 + 4 * 4 * 16 * 1024

@@ -5,7 +5,8 @@ and value distributions, and nothing else. It holds none of the attention
 arithmetic and imports neither the oracle nor the HIP binding.
 
 Recipe (every workload): a CPU ``torch.Generator`` seeded with the workload's
-seed draws Q, then K, then V as float32 standard normals of shape [B, H, N, d];
+seed draws Q, then K, then V as float32 standard normals of shape [B, H, N, d]
+(K and V [B, H, Nk, d] for a cross-attention workload);
 Q and K are multiplied by ``sigma_qk``, V by ``sigma_v``; the three tensors are
 then cast to the workload's element type (bf16 with round-to-nearest-even).
 Both the oracle and the GPU path consume exactly those cast values. The score
@@ -33,6 +34,11 @@ class Workload:
     seed: int
     sigma_qk: float = 1.0
     sigma_v: float = 1.0
+    Nk: int = 0  # key rows when they differ from the N query rows (0: Nk = N)
+
+    @property
+    def keys(self) -> int:
+        return self.Nk or self.N
 
     @property
     def torch_dtype(self):
@@ -43,13 +49,21 @@ class Workload:
         return default_scale(self.d)
 
     def make(self):
+        if self.Nk:
+            return make_qkv_cross(self.B, self.H, self.N, self.Nk, self.d, self.dtype, self.seed,
+                                  self.sigma_qk, self.sigma_v)
         return make_qkv(self.B, self.H, self.N, self.d, self.dtype, self.seed,
                         self.sigma_qk, self.sigma_v)
 
     def pairs(self) -> int:
-        """(query, key) pairs that enter the softmax: N^2, or N(N+1)/2 when causal."""
-        n = self.N
-        return n * (n + 1) // 2 if self.causal else n * n
+        """(query, key) pairs that enter the softmax per head: N Nk, or, when causal,
+        sum over queries i of min(i + 1, Nk) (N(N+1)/2 when Nk = N)."""
+        n, nk = self.N, self.keys
+        if not self.causal:
+            return n * nk
+        if nk >= n:
+            return n * (n + 1) // 2
+        return nk * (nk + 1) // 2 + (n - nk) * nk
 
     def flops(self) -> int:
         """Algorithmic FLOPs of the two contractions: 2d for Q.k plus 2d for p.v per pair."""
@@ -59,7 +73,8 @@ class Workload:
         """Algorithmic HBM bytes: read Q, K, V once, write O once and the fp32 L once."""
         esize = 2 if self.dtype == "bf16" else 4
         n = self.B * self.H * self.N
-        return 4 * n * self.d * esize + 4 * n
+        nk = self.B * self.H * self.keys
+        return 2 * (n + nk) * self.d * esize + 4 * n
 
 
 WORKLOADS = {
@@ -76,6 +91,9 @@ WORKLOADS = {
         # ragged N=1000, non-causal bf16, wide logits: Q, K ~ N(0, 4^2), V ~ N(0, 1)
         Workload("ragged_wide_logits_bf16_n1000", 2, 8, 1000, 128, "bf16", False, seed=5,
                  sigma_qk=4.0),
+        # cross-attention (through the strided entry point): 1024 queries over 4096 keys,
+        # non-causal bf16, B=4, H=16, d=128
+        Workload("cross_bf16_b4h16q1024k4096d128", 4, 16, 1024, 128, "bf16", False, seed=6, Nk=4096),
     ]
 }
 
