@@ -186,6 +186,70 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_per_dispatch": n * 4}), flush=True)
 
 
+def small_sweep(reps: int):
+    """The pages' small-shape sweep: per configuration, the median latency of one
+    fa_fwd call, of torch's scaled_dot_product_attention and of the explicit
+    softmax(Q K^T) V in torch, all fp32 on this GPU; one JSON line each."""
+    import statistics
+
+    import torch
+
+    import tiled_online_softmax_amd as fa
+    from workloads import SMALL_SWEEP
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    F = torch.nn.functional
+
+    def explicit(q, k, v, causal, scale):
+        s = torch.matmul(q, k.transpose(-1, -2).contiguous()) * scale
+        if causal:
+            n = s.shape[-1]
+            s = s.masked_fill(torch.ones(n, n, dtype=torch.bool, device=s.device).triu(1), float("-inf"))
+        return torch.matmul(torch.softmax(s, dim=-1), v)
+
+    def timed(fn):
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        dev_us, host_us = [], []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            host_us.append((time.perf_counter() - t0) * 1e6)
+            dev_us.append(a.elapsed_time(b) * 1e3)
+        return statistics.median(dev_us), statistics.median(host_us)
+
+    rows = []
+    for w in SMALL_SWEEP:
+        q, k, v = (t.to(dev) for t in w.make())
+        O = torch.empty_like(q)
+        L = torch.empty((1, 1, w.N), dtype=torch.float32, device=dev)
+        ours = timed(lambda: fa.fa_fwd(q, k, v, O, L, 1, 1, w.N, w.d, w.causal, w.scale, stream))
+        sdpa = timed(lambda: F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale))
+        expl = timed(lambda: explicit(q, k, v, w.causal, w.scale))
+        ref = F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
+        torch.cuda.synchronize()
+        rec = {"sweep": "small_shapes_f32", "workload": w.name, "N": w.N, "d": w.d, "causal": w.causal,
+               "fa_fwd_us": round(ours[0], 2), "sdpa_us": round(sdpa[0], 2), "explicit_us": round(expl[0], 2),
+               "fa_fwd_host_us": round(ours[1], 2), "sdpa_host_us": round(sdpa[1], 2),
+               "explicit_host_us": round(expl[1], 2),
+               "max_abs_diff_vs_sdpa": float((O - ref).abs().max()), "reps": reps}
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+    faster = sum(1 for r in rows if r["fa_fwd_us"] < r["sdpa_us"])
+    print(json.dumps({"sweep": "small_shapes_f32", "configs": len(rows), "fa_fwd_faster_than_sdpa": faster,
+                      "median_speedup_vs_sdpa": round(statistics.median(r["sdpa_us"] / r["fa_fwd_us"] for r in rows), 3),
+                      "timing": "median over reps of HIP events around one call on the current stream "
+                                "(*_host_us: host wall time of one call including launch and synchronisation)"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +263,8 @@ def main():
                     help="time the forward (default) or the backward pass")
     ap.add_argument("--layout", choices=("contiguous", "bshd"), default="contiguous",
                     help="forward only: bshd stores Q, K, V, O as [B, N, H, d] and calls fa_fwd_strided")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark, run the small-shape fp32 sweep against torch SDPA")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run three plain device copies of MIB MiB each "
                          "(reference dispatches for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -213,6 +279,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.sweep:
+        small_sweep(reps=200)
         return
 
     import tiled_online_softmax_amd as fa

@@ -100,6 +100,17 @@ WORKLOADS = {
 # The throughput workload: causal bf16, B=4, H=16, N=4096, d=128.
 HEADLINE = "causal_bf16_b4h16n4096d128"
 
+# The small-shape sweep of "Writing a FlashAttention kernel in Metal" (the benchmark
+# section): fp32, one sequence and one head, N in {64, 256, 1024, 2048}, d in {32, 64},
+# causal and not -- sixteen latency-bound configurations.
+SMALL_SWEEP = [
+    Workload(f"sweep_f32_n{n}_d{d}_{'causal' if causal else 'full'}", 1, 1, n, d, "f32", causal,
+             seed=100 + 8 * i + 2 * j + int(causal))
+    for i, n in enumerate((64, 256, 1024, 2048))
+    for j, d in enumerate((32, 64))
+    for causal in (False, True)
+]
+
 
 def torch_dtype(name: str):
     if name == "bf16":
