@@ -263,6 +263,8 @@ def main():
                     help="time the forward (default) or the backward pass")
     ap.add_argument("--layout", choices=("contiguous", "bshd"), default="contiguous",
                     help="forward only: bshd stores Q, K, V, O as [B, N, H, d] and calls fa_fwd_strided")
+    ap.add_argument("--specialize", action="store_true",
+                    help="forward only: call fa_fwd_specialized (kernel compiled at run time for this shape)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark, run the small-shape fp32 sweep against torch SDPA")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -289,6 +291,9 @@ def main():
 
     w = WORKLOADS[args.workload or HEADLINE]
     strided = args.layout == "bshd" or w.keys != w.N
+    if args.specialize and (strided or args.which == "bwd"):
+        print("--specialize applies to the contiguous forward pass", file=sys.stderr)
+        sys.exit(2)
     if args.which == "bwd" and strided:
         print("the backward pass takes contiguous [B, H, N, d] tensors with Nq = Nk", file=sys.stderr)
         sys.exit(2)
@@ -316,6 +321,14 @@ def main():
     elif strided:
         def step():
             fa.fa_fwd_strided(qd, kd, vd, O, L, w.causal, w.scale, stream)
+    elif args.specialize:
+        def step():
+            fa.fa_fwd_specialized(qd, kd, vd, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+
+        t_jit = time.perf_counter()
+        step()  # compiles and loads the kernel for this shape
+        torch.cuda.synchronize()
+        t_jit = time.perf_counter() - t_jit
     else:
         def step():
             fa.fa_fwd(qd, kd, vd, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
@@ -349,7 +362,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = None if (bwd or strided) else measured_traffic(w.name)
+    traffic = None if (bwd or strided or args.specialize) else measured_traffic(w.name)
     # backward: Q, K, V, O, dO read and dQ, dK, dV written once, plus L
     n_rows = w.B * w.H * w.N
     io_bytes = (2 * (w.io_bytes() - 4 * n_rows) + 4 * n_rows) if bwd else w.io_bytes()
@@ -387,6 +400,10 @@ def main():
     }
     if bwd:
         rec["roofline"]["kernel_ms"]["covers"] = "one fa_bwd call: preprocessing, dQ and dK/dV kernels"
+    if args.specialize:
+        rec["config"]["specialized"] = True
+        rec["jit_first_call_s"] = round(t_jit, 3)
+        rec["roofline"]["kernel_ms"]["covers"] = "one fa_fwd_specialized call (kernel compiled for this shape)"
     if strided:
         rec["config"]["Nk"] = w.keys
         rec["config"]["layout"] = args.layout

@@ -18,6 +18,7 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -30,7 +31,8 @@ typedef enum {
   FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, B/H/N < 1, scale not finite or <= 0, bad dtype */
   FA_ERR_UNSUPPORTED = 2,      /* head dimension not supported by the entry point, or a size too large */
   FA_ERR_MISALIGNED = 3,       /* a buffer not 16-byte aligned */
-  FA_ERR_LAUNCH = 4            /* the HIP runtime refused the kernel launch */
+  FA_ERR_LAUNCH = 4,           /* the HIP runtime refused the kernel launch */
+  FA_ERR_JIT = 5               /* run-time compilation or loading of a specialized kernel failed */
 } fa_status_t;
 
 /* Element type of Q, K, V and O. */
@@ -108,6 +110,41 @@ fa_status_t fa_fwd_strided(const void *Q, const void *K, const void *V, void *O,
                            const int64_t *v_strides, const int64_t *o_strides,
                            const int64_t *l_strides, int causal, float scale, void *stream,
                            int dtype);
+
+/*
+ * fa_fwd_specialized -- fa_fwd with the kernel compiled at run time for this
+ * exact shape: the sizes B, H, N (and the contiguous strides they imply)
+ * become compile-time constants, in the manner of the per-shape function
+ * constants of "Case Study: metal-flash-attention" (its sections on compiling
+ * a kernel per problem shape). Same arguments, semantics and validation as
+ * fa_fwd; the results agree with fa_fwd's within the fa_fwd tolerances.
+ *
+ * The first call for a (device, dtype, d, causal, B, H, N) compiles the
+ * forward kernel source embedded in the library with hipRTC (for gfx950, with
+ * the flags of the library's own build; about a second) and loads it on the
+ * current device; later calls reuse it. Loaded kernels are kept until the
+ * process ends. The cache is guarded by a mutex, so concurrent calls from
+ * several threads are safe; a call that compiles blocks its thread meanwhile.
+ * Returns FA_ERR_JIT if compiling or loading fails (nothing is enqueued).
+ */
+fa_status_t fa_fwd_specialized(const void *Q, const void *K, const void *V, void *O, float *L,
+                               int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                               void *stream, int dtype);
+
+/*
+ * fa_jit_code_object -- compile the kernel fa_fwd_specialized would load for
+ * (dtype, d, causal, B, H, N) and return its code object (an AMDGPU ELF for
+ * gfx950), without touching any GPU: for inspection or for callers that keep
+ * compiled kernels themselves.
+ *
+ *   buffer   host memory receiving the code object, or NULL to ask for its size.
+ *   size     in: the capacity of buffer; out: the code object's size in bytes.
+ * Returns FA_ERR_INVALID_ARGUMENT if size is NULL or the capacity is too small
+ * (*size then holds the size needed), FA_ERR_UNSUPPORTED / FA_ERR_INVALID_ARGUMENT
+ * for sizes and types fa_fwd rejects, FA_ERR_JIT if compilation fails.
+ */
+fa_status_t fa_jit_code_object(int dtype, int64_t d, int causal, int64_t B, int64_t H, int64_t N,
+                               void *buffer, size_t *size);
 
 /*
  * fa_bwd -- attention backward pass over B*H independent heads: the gradients

@@ -22,7 +22,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_strided", "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_specialized", "fa_fwd_strided", "fa_jit_code_object",
+                                    "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert fa.fa_status_string(0) == "ok"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert fa.fa_status_string(s) not in ("ok", "unknown status")
     assert fa.fa_status_string(99) == "unknown status"
     assert fa.fa_version() >= 100
@@ -197,3 +198,34 @@ def test_strided_fp32_alignment_unit():
     # check, so it is made to fail on the overlap check instead (O overlaps Q).
     assert call_strided(dtype=fa.FA_DTYPE_F32, q=(8192 * 2, 4096 * 2, 68), O=A + 64) == fa.FA_ERR_INVALID_ARGUMENT
     assert call_strided(dtype=fa.FA_DTYPE_F32, q=(8192, 4096, 66)) == fa.FA_ERR_MISALIGNED
+
+
+# fa_fwd_specialized validates exactly as fa_fwd, before compiling or launching anything.
+def call_spec(**kw):
+    a = dict(Q=A, K=2 * A, V=3 * A, O=4 * A, L=5 * A, B=1, H=1, N=64, d=64, causal=0, scale=0.125,
+             dtype=fa.FA_DTYPE_BF16)
+    a.update(kw)
+    return fa.raw_fa_fwd_specialized(a["Q"], a["K"], a["V"], a["O"], a["L"], a["B"], a["H"], a["N"], a["d"],
+                                     a["causal"], a["scale"], None, a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [(dict(Q=0), fa.FA_ERR_INVALID_ARGUMENT), (dict(N=0), fa.FA_ERR_INVALID_ARGUMENT),
+                                       (dict(scale=-1.0), fa.FA_ERR_INVALID_ARGUMENT), (dict(dtype=3), fa.FA_ERR_INVALID_ARGUMENT),
+                                       (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(O=2 * A + 64), fa.FA_ERR_INVALID_ARGUMENT),
+                                       (dict(K=2 * A + 8), fa.FA_ERR_MISALIGNED)])
+def test_specialized_validation(kw, status):
+    assert call_spec(**kw) == status
+
+
+def test_jit_code_object_arguments():
+    import ctypes
+
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    lib.fa_jit_code_object.restype = ctypes.c_int
+    lib.fa_jit_code_object.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 64, 0, 1, 1, 64, None, None) == fa.FA_ERR_INVALID_ARGUMENT
+    size = ctypes.c_size_t(0)
+    assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 96, 0, 1, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_jit_code_object(7, 64, 0, 1, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_INVALID_ARGUMENT
+    assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 64, 0, 0, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_INVALID_ARGUMENT

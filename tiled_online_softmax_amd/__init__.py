@@ -1,8 +1,8 @@
 """Tiled online-softmax attention forward and backward passes for MI355X (gfx950).
 
-``fa_fwd``, ``fa_fwd_strided`` and ``fa_bwd`` mirror the C entry points of
-``libfa.so``; ``forward``, ``forward_strided`` and ``backward`` allocate the outputs
-(and the backward workspace) and call them.
+``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_specialized`` and ``fa_bwd`` mirror the C
+entry points of ``libfa.so``; ``forward``, ``forward_strided``, ``forward_specialized``
+and ``backward`` allocate the outputs (and the backward workspace) and call them.
 Importing fails loudly when the HIP library is not built.
 """
 
@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     FA_DTYPE_BF16,
     FA_DTYPE_F32,
     FA_ERR_INVALID_ARGUMENT,
+    FA_ERR_JIT,
     FA_ERR_LAUNCH,
     FA_ERR_MISALIGNED,
     FA_ERR_UNSUPPORTED,
@@ -19,12 +20,16 @@ from ._binding import (  # noqa: F401
     backward,
     fa_bwd,
     fa_fwd,
+    fa_fwd_specialized,
     fa_fwd_strided,
     fa_status_string,
     fa_version,
     forward,
+    forward_specialized,
     forward_strided,
+    jit_code_object,
     raw_fa_bwd,
     raw_fa_fwd,
+    raw_fa_fwd_specialized,
     raw_fa_fwd_strided,
 )

@@ -21,6 +21,7 @@ FA_ERR_INVALID_ARGUMENT = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_MISALIGNED = 3
 FA_ERR_LAUNCH = 4
+FA_ERR_JIT = 5
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 
@@ -38,6 +39,11 @@ _lib.fa_fwd_strided.restype = ctypes.c_int
 _lib.fa_fwd_strided.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [ctypes.c_void_p] * 5 + [
     ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
 ]
+_lib.fa_fwd_specialized.restype = ctypes.c_int
+_lib.fa_fwd_specialized.argtypes = _lib.fa_fwd.argtypes
+_lib.fa_jit_code_object.restype = ctypes.c_int
+_lib.fa_jit_code_object.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
 _lib.fa_bwd.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -66,6 +72,24 @@ def fa_version() -> int:
 def raw_fa_fwd(Q, K, V, O, L, B, H, N, d, causal, scale, stream, dtype) -> int:
     """The C entry point with integer pointers; returns the status code."""
     return int(_lib.fa_fwd(Q, K, V, O, L, B, H, N, d, int(causal), float(scale), stream, int(dtype)))
+
+
+def raw_fa_fwd_specialized(Q, K, V, O, L, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """The shape-specialized C entry point with integer pointers; returns the status code."""
+    return int(_lib.fa_fwd_specialized(Q, K, V, O, L, B, H, N, d, int(causal), float(scale), stream, int(dtype)))
+
+
+def jit_code_object(dtype: int, d: int, causal: bool, B: int, H: int, N: int) -> bytes:
+    """The code object fa_fwd_specialized compiles for this shape (no GPU needed)."""
+    size = ctypes.c_size_t(0)
+    st = _lib.fa_jit_code_object(int(dtype), d, int(causal), B, H, N, None, ctypes.byref(size))
+    if st != FA_OK:
+        raise FaError(st, "fa_jit_code_object")
+    buf = ctypes.create_string_buffer(size.value)
+    st = _lib.fa_jit_code_object(int(dtype), d, int(causal), B, H, N, buf, ctypes.byref(size))
+    if st != FA_OK:
+        raise FaError(st, "fa_jit_code_object")
+    return buf.raw[: size.value]
 
 
 def _strides3(st):
@@ -167,6 +191,37 @@ def fa_fwd_strided(Q, K, V, O, L, causal, scale, stream=None):
                             causal, scale, _stream_handle(stream, Q.device), _DTYPES[dt])
     if st != FA_OK:
         raise FaError(st, "fa_fwd_strided")
+
+
+def fa_fwd_specialized(Q, K, V, O, L, B, H, N, d, causal, scale, stream=None):
+    """fa_fwd through the shape-specialized entry point (same checks as ``fa_fwd``)."""
+    dt = Q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for t in (Q, K, V, O):
+        if t.dtype != dt or tuple(t.shape) != (B, H, N, d) or not t.is_contiguous():
+            raise ValueError("Q, K, V, O must be contiguous [B, H, N, d] tensors of one dtype")
+        if t.device.type != "cuda" or t.device != Q.device:
+            raise ValueError("all tensors must live on the same GPU")
+    if L.dtype != torch.float32 or tuple(L.shape) != (B, H, N) or not L.is_contiguous() or L.device != Q.device:
+        raise ValueError("L must be a contiguous fp32 [B, H, N] tensor on the same GPU")
+    st = raw_fa_fwd_specialized(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), B, H, N, d, causal, scale,
+                                _stream_handle(stream, Q.device), _DTYPES[dt])
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_specialized")
+
+
+def forward_specialized(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate O (like q) and fp32 L, run fa_fwd_specialized, return (O, L)."""
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(d ** -0.5, dtype=torch.float32).item())
+    O = torch.empty_like(q)
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_specialized(q, k, v, O, L, B, H, N, d, causal, scale, stream)
+    return O, L
 
 
 def forward_strided(q, k, v, causal: bool = False, scale: float | None = None, stream=None):

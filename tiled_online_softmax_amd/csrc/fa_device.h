@@ -3,11 +3,20 @@
 #ifndef FA_DEVICE_H_
 #define FA_DEVICE_H_
 
+#if defined(__HIPCC_RTC__)
+// Run-time compilation (hipRTC) provides the HIP device builtins but not the C
+// headers: the fixed-width types and INFINITY come from the compiler itself.
+typedef __UINT32_TYPE__ uint32_t;
+typedef __INT64_TYPE__ int64_t;
+typedef __UINTPTR_TYPE__ uintptr_t;
+#define INFINITY (__builtin_inff())
+#else
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#endif
 
 namespace {
 
