@@ -43,14 +43,20 @@ def metric_name(which: str, w) -> str:
 # MI355X published dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x 4096 bf16 FLOP/clk/CU;
 # fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
-KERNEL_SOURCE = os.path.join(ROOT, "tiled_online_softmax_amd", "csrc", "fa_fwd.hip")
+# The forward kernel's sources: the device headers and the host source that launches them.
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_online_softmax_amd", "csrc", f)
+                  for f in ("fa_device.h", "fa_fwd_kernels.h", "fa_fwd.hip")]
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, per workload and kernel source.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_kernel_{}_traffic.json")
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the forward kernel's source files, in a fixed order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
