@@ -3,6 +3,47 @@
 // forward source and, as text, compiled at run time by hipRTC for the
 // shape-specialized entry point; it holds no host code.
 //
+// Computes O = softmax(scale * Q K^T) V per head, optionally causal, and the
+// per-row natural-log logsumexp L, without storing the N x N score matrix.
+//
+// Computes O = softmax(scale * Q K^T) V per head, optionally causal, and the
+// per-row natural-log logsumexp L, without storing the N x N score matrix.
+//
+// The method: "FlashAttention-2 from PyTorch to Triton", section "What We Are
+// Building" -- one workgroup per query tile, K/V tiles streamed past it, a
+// running row maximum m, running row sum l and an unnormalised output
+// accumulator that is rescaled by exp(m_old - m_new) on every key tile and
+// divided by l once at the end; L = m + log l. The recurrence itself is the one
+// derived in "Writing a FlashAttention kernel in Metal", sections "Online
+// softmax", "One-query attention" and "Blockwise attention and causal
+// masking"; the base-2 form with the guarded correction factor follows the
+// softmax fragment of "Case Study: metal-flash-attention".
+//
+// gfx950 mapping (see the layout comments at each step):
+//  * bf16: a workgroup of four wave64s owns 128 query rows; each wave owns 32
+//    rows and keeps its Q rows in VGPRs for the whole key loop. fp32: a
+//    workgroup owns 32 query rows and its waves split the key tiles, merging
+//    their partial (m, l, O) through LDS at the end.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+//    (bf16) or v_mfma_f32_32x32x2_f32 (fp32). In the result layout a lane holds
+//    16 keys of ONE query, so the row maximum and row sum are 16 in-lane ops
+//    plus one v_permlane32_swap between the two half-waves, and the running
+//    state m, l is a per-lane scalar.
+//  * The same registers, converted to bf16, are the B operand of the second
+//    contraction O^T += V^T P^T with no data movement; V^T comes straight out
+//    of LDS with ds_read_b64_tr_b16 (transposing 4-key x 16-column blocks).
+//  * bf16: K/V tiles of 64 keys are copied global -> LDS (XOR-swizzled rows),
+//    K two tiles and V one tile ahead of their use. fp32: each wave loads its
+//    32-key K/V operands straight into VGPRs, the next tile's loads in flight
+//    while the current tile is computed.
+//  * Scores are scaled into the base-2 domain (scale * log2 e folded into one
+//    FMA) and exponentiated with v_exp_f32.
+//  * Causal: key tiles wholly after the query tile are never loaded, 32-key
+//    blocks wholly after a wave's rows are skipped by that wave, and the mask
+//    is evaluated only on blocks that straddle the diagonal or the ragged end.
+//  * The workgroup index is remapped so that the eight XCDs each own whole
+//    heads (their L2 keeps that head's K/V), heaviest causal tiles first.
+//
 // Shape specialization: when FA_SPEC_NQ is defined (hipRTC builds), the row
 // counts, the batch and head counts and the strides of a contiguous
 // [B][H][N][d] layout are compile-time constants (FA_SPEC_B, FA_SPEC_H,
