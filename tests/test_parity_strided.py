@@ -169,3 +169,38 @@ def test_cross_workload_full_size(fa, layout):
         sl = (slice(b, b + 1), slice(h, h + 1))
         Oref, Lref = _oracle_cross(q[sl], k[sl], v[sl], w.causal, w.scale)
         _compare(O[sl], L[sl], Oref, Lref, "bf16", f"cross workload {layout} head ({b},{h})")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [16, 128])
+def test_strided_outputs_and_lse(fa, d, dtype):
+    """O written into a [B, N, H, d] view and L into every other float of a wider buffer,
+    with Nq > Nk, causal (queries past Nk see every key)."""
+    B, H, Nq, Nk = 2, 3, 190, 70
+    q, k, v = make_qkv_cross(B, H, Nq, Nk, d, dtype, seed=4000 + d)
+    scale = default_scale(d)
+    O = torch.full((B, Nq, H, d), float("nan"), dtype=q.dtype, device=DEV).transpose(1, 2)
+    Lbuf = torch.full((B, H, 2 * Nq), float("nan"), dtype=torch.float32, device=DEV)
+    L = Lbuf[:, :, ::2]
+    fa.fa_fwd_strided(q.to(DEV), k.to(DEV), v.to(DEV), O, L, True, scale)
+    torch.cuda.synchronize()
+    Oref, Lref = _oracle_cross(q, k, v, True, scale)
+    _compare(O, L, Oref, Lref, dtype, f"strided O/L {dtype} d={d}")
+    assert torch.isnan(Lbuf[:, :, 1::2]).all(), "L stride: the skipped floats were written"
+
+
+def test_strided_zero_batch_stride_inputs(fa):
+    """K and V shared by both batches (batch stride 0) and Q heads broadcast from one head."""
+    B, H, Nq, Nk, d = 2, 4, 96, 160, 64
+    q1, k1, v1 = make_qkv_cross(1, 1, Nq, Nk, d, "bf16", seed=4100)
+    qd = q1.to(DEV).expand(B, H, Nq, d)
+    kd = k1.to(DEV).expand(B, H, Nk, d)
+    vd = v1.to(DEV).expand(B, H, Nk, d)
+    O = torch.empty((B, H, Nq, d), dtype=q1.dtype, device=DEV)
+    L = torch.empty((B, H, Nq), dtype=torch.float32, device=DEV)
+    fa.fa_fwd_strided(qd, kd, vd, O, L, False, default_scale(d))
+    torch.cuda.synchronize()
+    Oref, Lref = _oracle_cross(q1, k1, v1, False, default_scale(d))
+    for b in range(B):
+        for h in range(H):
+            _compare(O[b:b + 1, h:h + 1], L[b:b + 1, h:h + 1], Oref, Lref, "bf16", f"broadcast ({b},{h})")
