@@ -167,6 +167,8 @@ def test_strided_bad_sizes(kw):
     dict(o=(0, 4096, 64), B=2),         # two batches of O at one address
     dict(l=(128, 0, 1)),                # both heads of L at one address
     dict(O=2 * A + 64),                 # O overlaps K
+    dict(B=1 << 30, H=1, q=(1 << 40, 4096, 64), k=(1 << 40, 6144, 64), v=(1 << 40, 6144, 64),
+         o=(1 << 40, 4096, 64), l=(1 << 20, 64, 1)),  # spans past 2^62 bytes
     dict(L=4 * A + 64),                 # L overlaps O
 ])
 def test_strided_invalid_layouts(kw):

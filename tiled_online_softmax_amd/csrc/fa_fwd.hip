@@ -107,10 +107,27 @@ bool supported_sizes(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk) {
 struct Span {
   uintptr_t lo, hi;
 };
+// Elements from the first to one past the last element of the array, or
+// false if that count (times the element size) does not fit in 2^62.
+bool element_extent(int64_t B, int64_t H, int64_t rows, int64_t inner, const int64_t st[3], size_t esize,
+                    int64_t *extent) {
+  const int64_t ext[3] = {B, H, rows};
+  int64_t total = inner;
+  for (int i = 0; i < 3; ++i) {
+    int64_t step;
+    if (__builtin_mul_overflow(ext[i] - 1, st[i], &step) || __builtin_add_overflow(total, step, &total))
+      return false;
+  }
+  int64_t bytes;
+  if (__builtin_mul_overflow(total, (int64_t)esize, &bytes) || bytes > ((int64_t)1 << 62)) return false;
+  *extent = total;
+  return true;
+}
 Span tensor_span(const void *base, int64_t B, int64_t H, int64_t rows, int64_t inner, const int64_t st[3],
                  size_t esize) {
-  const int64_t last = (B - 1) * st[0] + (H - 1) * st[1] + (rows - 1) * st[2] + inner;
-  return {(uintptr_t)base, (uintptr_t)base + (uintptr_t)last * esize};
+  int64_t extent = 0;
+  element_extent(B, H, rows, inner, st, esize, &extent);  // checked by the caller
+  return {(uintptr_t)base, (uintptr_t)base + (uintptr_t)extent * esize};
 }
 bool spans_overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
@@ -132,7 +149,9 @@ bool non_overlapping(int64_t B, int64_t H, int64_t rows, int64_t inner, const in
   for (int i = 0; i < 3; ++i) {
     if (ext[i] == 1) continue;
     if (str[i] < span) return false;
-    span += (ext[i] - 1) * str[i];
+    int64_t step;
+    if (__builtin_mul_overflow(ext[i] - 1, str[i], &step) || __builtin_add_overflow(span, step, &span))
+      return false;
   }
   return true;
 }
@@ -332,6 +351,15 @@ extern "C" fa_status_t fa_fwd_strided(const void *Q, const void *K, const void *
   if (!non_overlapping(B, H, Nq, d, o_strides) || !non_overlapping(B, H, Nq, 1, l_strides))
     return FA_ERR_INVALID_ARGUMENT;
   const size_t esize = dtype == FA_DTYPE_BF16 ? 2 : 4;
+  {
+    int64_t extent;
+    if (!element_extent(B, H, Nq, d, q_strides, esize, &extent) ||
+        !element_extent(B, H, Nk, d, k_strides, esize, &extent) ||
+        !element_extent(B, H, Nk, d, v_strides, esize, &extent) ||
+        !element_extent(B, H, Nq, d, o_strides, esize, &extent) ||
+        !element_extent(B, H, Nq, 1, l_strides, sizeof(float), &extent))
+      return FA_ERR_INVALID_ARGUMENT;  // an array spans more than 2^62 bytes
+  }
   if (!supported_head_dim(d)) return FA_ERR_UNSUPPORTED;
   if (!supported_sizes(dtype, B, H, Nq, Nk)) return FA_ERR_UNSUPPORTED;
   for (const int64_t *st : ts)
