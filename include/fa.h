@@ -167,7 +167,8 @@ fa_status_t fa_jit_code_object(int dtype, int64_t d, int causal, int64_t B, int6
  *            sum over c of dO*O, then L * log2 e). Owned by the caller; its
  *            contents after the call carry no meaning.
  *   B,H,N, causal, scale, stream: as for fa_fwd.
- *   d        64 or 128 (16 and 32 return FA_ERR_UNSUPPORTED).
+ *   d        64 or 128; with FA_DTYPE_F32 also 32. Other values return
+ *            FA_ERR_UNSUPPORTED.
  *   dtype    FA_DTYPE_BF16 or FA_DTYPE_F32 (all of Q, K, V, O, dO and the
  *            gradients in that type).
  *

@@ -111,7 +111,7 @@ def test_bwd_bad_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(d=32), dict(d=96), dict(N=(1 << 24) + 1),
-                                dict(d=96, dtype=fa.FA_DTYPE_F32)])
+                                dict(d=96, dtype=fa.FA_DTYPE_F32), dict(d=16, dtype=fa.FA_DTYPE_F32)])
 def test_bwd_unsupported(kw):
     assert call_bwd(**kw) == fa.FA_ERR_UNSUPPORTED
 

@@ -135,6 +135,14 @@ def test_bwd_f32_heads(fa, B, H, N, d, causal):
     _check(fa, q, k, v, do, causal, default_scale(d), f"f32 B={B} H={H} N={N} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 64, 100, 257, 1024])
+def test_bwd_f32_d32(fa, N, causal):
+    """fp32 at d = 32 (the head dimension of the small-shape sweep)."""
+    q, k, v, do = _inputs(1, 2, N, 32, seed=3100 + N, dtype="f32")
+    _check(fa, q, k, v, do, causal, default_scale(32), f"f32 d=32 N={N} causal={causal}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_f32_long_sequence(fa, d):
     """N = 4100: 129 tiles per workgroup (each wave takes every fourth), a ragged last one."""

@@ -838,9 +838,10 @@ extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARGUMENT;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (N > (int64_t)1 << 24) return FA_ERR_UNSUPPORTED;
   const bool bf = dtype == FA_DTYPE_BF16;
+  // bf16: d = 64, 128 (the 8-wave dK/dV tile loads need 8 KiB tiles); fp32 also d = 32.
+  if (d != 64 && d != 128 && !(d == 32 && !bf)) return FA_ERR_UNSUPPORTED;
+  if (N > (int64_t)1 << 24) return FA_ERR_UNSUPPORTED;
   const int64_t block_rows = bf ? kBwdRows : kF32Block;
   const int64_t ntiles = (N + block_rows - 1) / block_rows;
   if (B * H > ((int64_t)1 << 31) / ntiles - 1) return FA_ERR_UNSUPPORTED;
@@ -879,7 +880,10 @@ extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const
       err = causal ? launch_bwd_bf16<128, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
                    : launch_bwd_bf16<128, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
   } else {
-    if (d == 64)
+    if (d == 32)
+      err = causal ? launch_bwd_f32<32, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
+                   : launch_bwd_f32<32, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
+    else if (d == 64)
       err = causal ? launch_bwd_f32<64, true>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale)
                    : launch_bwd_f32<64, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
     else
