@@ -120,6 +120,51 @@ def test_edge_sizes(fa, N, causal, d, dtype):
     _check(fa, q, k, v, causal, default_scale(d), dtype, label=f"N={N} d={d} causal={causal} {dtype}")
 
 
+def _check_repeated(fa, q, k, v, causal, reps, label):
+    """The heads of q, k, v, and the same heads repeated `reps` times in one launch: both
+    match the oracle (computed once, on the distinct heads), and every repeat of a head is
+    bitwise identical to its first copy."""
+    dev = torch.device("cuda:0")
+    scale = default_scale(q.shape[-1])
+    H = q.shape[1]
+    Oref, Lref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
+    otol, ltol = TOL["bf16"]
+    for r in (1, reps):
+        qd, kd, vd = (t.repeat(1, r, 1, 1).to(dev) for t in (q, k, v))
+        O, L = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        eo, el = _errors(O[:, :H], L[:, :H], Oref, Lref)
+        print(f"[parity] {label} x{r} max|dO|={eo:.3e} max|dL|={el:.3e}", flush=True)
+        assert eo <= otol and el <= ltol, f"{label} x{r}: O error {eo}, L error {el}"
+        for j in range(1, r):
+            assert torch.equal(O[:, j * H:(j + 1) * H], O[:, :H]) and torch.equal(L[:, j * H:(j + 1) * H], L[:, :H])
+
+
+KS_N = [1, 17, 33, 63, 64, 65, 127, 129, 255, 1000]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("N", KS_N)
+def test_bf16_small_and_large_grid(fa, N, causal, d):
+    """bf16 launches of at most 192 workgroups of 128 query rows (B*H*ceil(N/128) <= 192)
+    pair the waves of a workgroup over the keys of each tile; larger ones give every wave
+    all keys of its 32 rows. Two heads run alone (the paired form) and repeated to 194
+    heads (the other form, at least 194 workgroups)."""
+    q, k, v = make_qkv(1, 2, N, d, "bf16", seed=3000 + N + d)
+    _check_repeated(fa, q, k, v, causal, 97, f"N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_grid_size_threshold(fa, causal):
+    """One head repeated to 192 heads (192 workgroups of 128 rows: paired waves) and 193
+    (one wave per 32 rows over all keys), N = 100 and N = 128 (one tile)."""
+    for N in (100, 128):
+        q, k, v = make_qkv(1, 1, N, 128, "bf16", seed=3100 + N)
+        for reps in (192, 193):
+            _check_repeated(fa, q, k, v, causal, reps, f"N={N} heads={reps} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_grid_not_multiple_of_xcds(fa, causal):
     """B*H*tiles = 3*37*2 = 222 workgroups: the XCD renumbering must stay a bijection."""

@@ -48,8 +48,29 @@ constexpr int kBf16Keys = FA_BF16_BN;
 
 constexpr int kBf16Rows = kRowsPerWave * kBf16Waves;  // query rows per workgroup
 
+// Compute units of the MI355X (gfx950).
+constexpr int64_t kComputeUnits = 256;
+
+// Key split of the bf16 kernel for small grids: when one workgroup per 128
+// query rows would leave at least a quarter of the compute units idle, the
+// kernel runs with its waves paired over the key blocks of each tile (64 query
+// rows per workgroup, twice the workgroups, half the keys per wave).
+constexpr int kBf16SmallGridSplit = 2;
+bool bf16_small_grid(int64_t BH, int64_t Nq) {
+  return 4 * BH * ((Nq + kBf16Rows - 1) / kBf16Rows) <= 3 * kComputeUnits;
+}
+int64_t bf16_rows(int64_t BH, int64_t Nq) {
+  return bf16_small_grid(BH, Nq) ? kBf16Rows / kBf16SmallGridSplit : kBf16Rows;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bf16(int64_t BH, hipStream_t s, FwdParams p) {
+  if (bf16_small_grid(BH, p.Nq)) {
+    constexpr int rows = kBf16Rows / kBf16SmallGridSplit;
+    p.n_qtiles = (p.Nq + rows - 1) / rows;
+    const void *kern = (const void *)&fa_fwd_bf16_kernel<D, CAUSAL, kBf16Waves, kBf16Keys, kBf16SmallGridSplit>;
+    return launch(kern, BH * p.n_qtiles, 64 * kBf16Waves, s, p);
+  }
   p.n_qtiles = (p.Nq + kBf16Rows - 1) / kBf16Rows;
   const void *kern = (const void *)&fa_fwd_bf16_kernel<D, CAUSAL, kBf16Waves, kBf16Keys>;
   return launch(kern, BH * p.n_qtiles, 64 * kBf16Waves, s, p);
@@ -213,14 +234,17 @@ FwdParams contiguous_params(const void *Q, const void *K, const void *V, void *O
 // (FA_SPEC_*, see fa_fwd_kernels.h), with the flags of the ahead-of-time build,
 // and the code object is loaded once per device and kept for the process.
 
-int block_rows(int dtype) { return dtype == FA_DTYPE_BF16 ? kBf16Rows : kF32Rows; }
+// Query rows per workgroup and threads per workgroup of the kernel that
+// launch_bf16 / launch_f32 pick for this shape.
+int64_t block_rows(int dtype, int64_t BH, int64_t N) { return dtype == FA_DTYPE_BF16 ? bf16_rows(BH, N) : kF32Rows; }
 int block_threads(int dtype) { return 64 * (dtype == FA_DTYPE_BF16 ? kBf16Waves : kF32Waves); }
 
-std::string kernel_expression(int dtype, int64_t d, int causal) {
+std::string kernel_expression(int dtype, int64_t d, int causal, int64_t BH, int64_t N) {
   const std::string c = causal ? "true" : "false";
   if (dtype == FA_DTYPE_BF16)
     return "fa_fwd_bf16_kernel<" + std::to_string(d) + ", " + c + ", " + std::to_string(kBf16Waves) + ", " +
-           std::to_string(kBf16Keys) + ">";
+           std::to_string(kBf16Keys) + ", " + std::to_string(bf16_small_grid(BH, N) ? kBf16SmallGridSplit : 1) +
+           ">";
   return "fa_fwd_f32_kernel<" + std::to_string(d) + ", " + c + ", " + std::to_string(kF32Waves) + ">";
 }
 
@@ -232,7 +256,7 @@ fa_status_t jit_compile(int dtype, int64_t d, int causal, int64_t B, int64_t H, 
   if (hiprtcCreateProgram(&prog, "#include \"fa_fwd_kernels.h\"\n", "fa_fwd_specialized.hip", kJitNumSources,
                           kJitSources, kJitSourceNames) != HIPRTC_SUCCESS)
     return FA_ERR_JIT;
-  const std::string expr = kernel_expression(dtype, d, causal);
+  const std::string expr = kernel_expression(dtype, d, causal, B * H, N);
   const std::vector<std::string> opts = {
       "--offload-arch=gfx950", "-O3", "-std=c++17",
       "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -300,7 +324,8 @@ extern "C" fa_status_t fa_fwd_specialized(const void *Q, const void *K, const vo
     kern = it->second;
   }
   FwdParams p = contiguous_params(Q, K, V, O, L, H, N, d, scale);
-  p.n_qtiles = (int)((N + block_rows(dtype) - 1) / block_rows(dtype));
+  const int64_t rows = block_rows(dtype, B * H, N);
+  p.n_qtiles = (int)((N + rows - 1) / rows);
   void *args[] = {(void *)&p};
   const hipError_t err = hipModuleLaunchKernel(kern.function, (unsigned)(B * H * p.n_qtiles), 1, 1,
                                                (unsigned)block_threads(dtype), 1, 1, 0, (hipStream_t)stream,

@@ -6,9 +6,6 @@
 // Computes O = softmax(scale * Q K^T) V per head, optionally causal, and the
 // per-row natural-log logsumexp L, without storing the N x N score matrix.
 //
-// Computes O = softmax(scale * Q K^T) V per head, optionally causal, and the
-// per-row natural-log logsumexp L, without storing the N x N score matrix.
-//
 // The method: "FlashAttention-2 from PyTorch to Triton", section "What We Are
 // Building" -- one workgroup per query tile, K/V tiles streamed past it, a
 // running row maximum m, running row sum l and an unnormalised output
@@ -21,7 +18,8 @@
 //
 // gfx950 mapping (see the layout comments at each step):
 //  * bf16: a workgroup of four wave64s owns 128 query rows; each wave owns 32
-//    rows and keeps its Q rows in VGPRs for the whole key loop. fp32: a
+//    rows and keeps its Q rows in VGPRs for the whole key loop (grids too small
+//    to fill the chip: 64 rows, two waves per 32 rows splitting the keys). fp32: a
 //    workgroup owns 32 query rows and its waves split the key tiles, merging
 //    their partial (m, l, O) through LDS at the end.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
@@ -141,12 +139,22 @@ constexpr float kRescaleSlack = 8.0f;
 // D < 32 (d = 16) runs on the layout of D = 32: the missing columns of the K
 // and V tiles are filled with zeros by out-of-range loads, Q's with zeros, and
 // the extra output columns are not stored.
-template <int D, bool CAUSAL, int NW, int BN>
+//
+// Key split KS > 1 (for grids too small to occupy every compute unit): the
+// waves form NW / KS groups of 32 query rows, and wave ks of a group takes the
+// 32-key blocks ks, ks + KS, ... of every tile; all waves still load and share
+// the same LDS tiles. Each wave keeps its own (m, l, O) over its keys, and at
+// the end the other waves of a group hand theirs to wave 0 of the group through
+// LDS, which merges them by the rule that combines two key blocks (rescale each
+// by exp2 of its reference maximum minus the larger one, then add).
+template <int D, bool CAUSAL, int NW, int BN, int KS = 1>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(const FwdParams p) {
   constexpr int DP = D < 32 ? 32 : D;    // head dimension of the tile layout
   using LY = BfLayout<DP, BN, NW>;
-  constexpr int BM = kRowsPerWave * NW;  // query rows per workgroup
   constexpr int NKB = BN / 32;           // 32-key MFMA blocks per tile
+  static_assert(NW % KS == 0 && NKB % KS == 0, "the key split divides the waves and the blocks of a tile");
+  constexpr int NKW = NKB / KS;          // 32-key blocks per tile of one wave
+  constexpr int BM = kRowsPerWave * (NW / KS);  // query rows per workgroup
   constexpr int NDB = DP / 32;           // 32-column blocks of the output
   constexpr int NCC = DP / 16;           // 16-wide steps of the score contraction
   __shared__ __attribute__((aligned(1024))) char smem[2 * LY::STAGE];
@@ -167,7 +175,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
   const bf16 *Vh = (const bf16 *)p.V + b * sh.v_b + h * sh.v_h;
 
   const int q0 = qt * BM;
-  const int qw = q0 + kRowsPerWave * wave;  // first query row of this wave
+  const int ks = KS == 1 ? 0 : wave % KS;         // this wave's share of the key blocks
+  const int qw = q0 + kRowsPerWave * (wave / KS);  // first query row of this wave
   const int qrow = qw + l32;                // the query row this lane carries
   const bool wave_live = qw < Nq;           // wave has rows to compute (uniform)
 
@@ -203,14 +212,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
   };
 
   // K reads (A operand of S^T = K Q^T): row 32kb + l32, chunk 2cc + hh; the
-  // chunk index only flips bits 5..7 of the byte address.
-  const int kbase = l32 * LY::ROW + 16 * (hh ^ LY::swz_k(l32));
+  // chunk index only flips bits 5..7 of the byte address. Both swizzles repeat
+  // every 32 rows, so the wave's first block (32 ks rows in) is a plain offset.
+  const int kbase = (32 * ks + l32) * LY::ROW + 16 * (hh ^ LY::swz_k(l32));
   // V transposing reads: 16-lane group g reads rows 4hh + (lane%16)/4 (+8u, +16mm,
   // +32kb) and columns 32db + 16(g%2) + 4(lane%4); in slot terms the column block
   // db is XORed with swz_v(row)/4.
   const int vrow = 4 * hh + (lane % 16) / 4;
   const int vchunk = 2 * ((lane / 16) % 2) + (lane % 4) / 2;  // chunk within a 32-column block
-  const int vbase = vrow * LY::ROW + 16 * (vchunk ^ LY::swz_v(vrow)) + 8 * (lane % 2);
+  const int vbase = (32 * ks + vrow) * LY::ROW + 16 * (vchunk ^ LY::swz_v(vrow)) + 8 * (lane % 2);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16cc + 8hh + 0..7]
   // (zeros past row Nq or column D).
@@ -234,19 +244,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
   // Leading tiles that need no mask for any row of the workgroup.
   const int nfull = CAUSAL ? min((q0 + 1) / BN, Nk / BN) : Nk / BN;
 
-  // Is 32-key block kb of tile t needed by this wave? (always, off the edge)
+  // First key of this wave's block kb (of NKW) in tile t.
+  auto block_key = [&](int t, int kb) { return t * BN + 32 * (KS * kb + ks); };
+  // Is this wave's block kb of tile t needed by the wave? (always, off the edge)
   auto block_live = [&](int t, int kb) {
-    const int kb0 = t * BN + 32 * kb;
+    const int kb0 = block_key(t, kb);
     return kb0 < Nk && (!CAUSAL || kb0 <= qw + kRowsPerWave - 1);
   };
 
   // S^T blocks of 32 keys x 32 queries for tile t. Result layout: lane (l32, hh),
   // register r holds key 8(r/4) + 4hh + r%4 of the block, query qrow.
-  auto scores = [&](int t, f32x16 (&s)[NKB], auto edge_tag) {
+  auto scores = [&](int t, f32x16 (&s)[NKW], auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const char *ks = smem + (t & 1) * LY::STAGE;
+    const char *kt = smem + (t & 1) * LY::STAGE;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKW; ++kb) {
       if (EDGE && !block_live(t, kb)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
@@ -254,15 +266,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
       }
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) {
-        const bf16x8 a = *(const bf16x8 *)(ks + 32 * kb * LY::ROW + (kbase ^ (32 * cc)));
+        const bf16x8 a = *(const bf16x8 *)(kt + 32 * KS * kb * LY::ROW + (kbase ^ (32 * cc)));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc == 0 ? f32x16{} : s[kb], 0, 0, 0);
       }
     }
   };
-  auto mask = [&](int t, f32x16 (&s)[NKB]) {
+  auto mask = [&](int t, f32x16 (&s)[NKW]) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int kb0 = t * BN + 32 * kb;
+    for (int kb = 0; kb < NKW; ++kb) {
+      const int kb0 = block_key(t, kb);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb0 + 8 * (r / 4) + 4 * hh + (r % 4);
@@ -271,10 +283,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
       }
     }
   };
-  auto rowmax = [&](const f32x16 (&s)[NKB]) {
+  auto rowmax = [&](const f32x16 (&s)[NKW]) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKW; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     return halves_max(mx);
@@ -298,38 +310,38 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
   };
   // P = exp2(S c - m) in place, and its bf16 copy as the B operand (P^T) of the
   // second MFMA: key half mm of block kb is registers 8mm..8mm+7 of s[kb].
-  auto exponentiate = [&](f32x16 (&s)[NKB], bf16x8 (&pb)[NKB][2]) {
+  auto exponentiate = [&](f32x16 (&s)[NKW], bf16x8 (&pb)[NKW][2]) {
     const float mref = (m == -INFINITY) ? 0.f : m;  // no -inf - -inf
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKW; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = exp2_fast(fmaf(s[kb][r], c, -mref));
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKW; ++kb)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) pb[kb][mm][t8] = (bf16)s[kb][8 * mm + t8];
   };
-  auto rowsum = [&](const f32x16 (&s)[NKB]) {
+  auto rowsum = [&](const f32x16 (&s)[NKW]) {
     float ps = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKW; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ps += s[kb][r];
     return ps;
   };
   // O^T += V^T P^T for tile t. The A operand (V^T) lists the keys of P's slots
   // 16mm + 8(t/4) + 4hh + t%4 via two transposing reads of 4 consecutive keys.
-  auto accumulate = [&](int t, const bf16x8 (&pb)[NKB][2], auto edge_tag) {
+  auto accumulate = [&](int t, const bf16x8 (&pb)[NKW][2], auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const char *vs = smem + (t & 1) * LY::STAGE + LY::TILE;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NKW; ++kb) {
       if (EDGE && !block_live(t, kb)) continue;
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
-        const int roff = (32 * kb + 16 * mm) * LY::ROW;
+        const int roff = (32 * KS * kb + 16 * mm) * LY::ROW;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const char *p0 = vs + roff + (vbase ^ (64 * db));
@@ -353,23 +365,23 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
   // The steady-state form (both tiles full, a next tile exists) is straight-line
   // code; the generic form, used for the few tiles at the diagonal or the
   // ragged end, tests its conditions at run time (all uniform).
-  auto iteration_full = [&](int t, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB]) {
+  auto iteration_full = [&](int t, f32x16 (&s_cur)[NKW], f32x16 (&s_nxt)[NKW]) {
     publish();
     if (t + 2 < nt) issue_k(t + 2);
     issue_v(t + 1);
-    bf16x8 pb[NKB][2];
+    bf16x8 pb[NKW][2];
     scores(t + 1, s_nxt, std::false_type{});
     exponentiate(s_cur, pb);
     accumulate(t, pb, std::false_type{});
     lsum += rowsum(s_cur);
     update_ref(rowmax(s_nxt));
   };
-  auto iteration_edge = [&](int t, f32x16 (&s_cur)[NKB], f32x16 (&s_nxt)[NKB]) {
+  auto iteration_edge = [&](int t, f32x16 (&s_cur)[NKW], f32x16 (&s_nxt)[NKW]) {
     const bool has_next = t + 1 < nt;
     publish();
     if (t + 2 < nt) issue_k(t + 2);
     if (has_next) issue_v(t + 1);
-    bf16x8 pb[NKB][2];
+    bf16x8 pb[NKW][2];
     if (has_next) scores(t + 1, s_nxt, std::true_type{});
     exponentiate(s_cur, pb);
     accumulate(t, pb, std::true_type{});
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
     }
   };
 
-  f32x16 sa[NKB], sb[NKB];
+  f32x16 sa[NKW], sb[NKW];
   // Prologue: K(0), V(0), K(1) in flight; S(0) and its reference maximum.
   issue_k(0);
   issue_v(0);
@@ -409,6 +421,60 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
   for (; t < nt; t += 2) {
     iteration_edge(t, sa, sb);
     if (t + 1 < nt) iteration_edge(t + 1, sb, sa);
+  }
+
+  if constexpr (KS > 1) {
+    // Hand-over area: for wave (group g, share j >= 1), NDB x 4 f32x4 of O per
+    // lane (lane-contiguous, conflict-free), then m and l per lane. The tiles
+    // are dead: no loads are in flight after the last iteration.
+    constexpr int SLOT = (16 * NDB + 2) * 64;  // floats per handing wave
+    static_assert((NW / KS) * (KS - 1) * SLOT * 4 <= 2 * LY::STAGE, "hand-over fits in the tile buffers");
+    float *xs = (float *)smem;
+    const int g = wave / KS;
+    __syncthreads();  // every wave is done reading the tiles
+    if (ks != 0) {
+      float *slot = xs + (g * (KS - 1) + ks - 1) * SLOT;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[db][4 * q4 + e];
+          *(f32x4 *)(slot + 4 * ((4 * db + q4) * 64 + lane)) = v;
+        }
+      slot[16 * NDB * 64 + lane] = m;
+      slot[16 * NDB * 64 + 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (ks != 0) return;
+    // Share 0 has a live key in every tile it visits (the tile's first key is
+    // at or before every row of the group), so m is finite; a share that saw
+    // no live key has m = -inf and weight exp2(-inf) = 0.
+    float mt = m;
+#pragma unroll
+    for (int j = 1; j < KS; ++j) mt = fmaxf(mt, xs[(g * (KS - 1) + j - 1) * SLOT + 16 * NDB * 64 + lane]);
+    const float f0 = exp2_fast(m - mt);
+    lsum *= f0;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= f0;
+#pragma unroll
+    for (int j = 1; j < KS; ++j) {
+      const float *slot = xs + (g * (KS - 1) + j - 1) * SLOT;
+      const float fj = exp2_fast(slot[16 * NDB * 64 + lane] - mt);
+      lsum = fmaf(slot[16 * NDB * 64 + 64 + lane], fj, lsum);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = *(const f32x4 *)(slot + 4 * ((4 * db + q4) * 64 + lane));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][4 * q4 + e] = fmaf(v[e], fj, o[db][4 * q4 + e]);
+        }
+    }
+    m = mt;
   }
 
   if (!wave_live) return;
