@@ -147,21 +147,23 @@ KS_N = [1, 17, 33, 63, 64, 65, 127, 129, 255, 1000]
 @pytest.mark.parametrize("d", [16, 64, 128])
 @pytest.mark.parametrize("N", KS_N)
 def test_bf16_small_and_large_grid(fa, N, causal, d):
-    """bf16 launches of at most 192 workgroups of 128 query rows (B*H*ceil(N/128) <= 192)
-    pair the waves of a workgroup over the keys of each tile; larger ones give every wave
-    all keys of its 32 rows. Two heads run alone (the paired form) and repeated to 194
-    heads (the other form, at least 194 workgroups)."""
+    """bf16 launches of at most 192 workgroups of 128 query rows (B*H*ceil(N/128) <= 192;
+    384 when causal) pair the waves of a workgroup over the keys of each tile; larger ones
+    give every wave all keys of its 32 rows. Two heads run alone (the paired form) and
+    repeated to 400 heads (the other form, at least 400 workgroups)."""
     q, k, v = make_qkv(1, 2, N, d, "bf16", seed=3000 + N + d)
-    _check_repeated(fa, q, k, v, causal, 97, f"N={N} d={d} causal={causal}")
+    _check_repeated(fa, q, k, v, causal, 200, f"N={N} d={d} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_grid_size_threshold(fa, causal):
-    """One head repeated to 192 heads (192 workgroups of 128 rows: paired waves) and 193
-    (one wave per 32 rows over all keys), N = 100 and N = 128 (one tile)."""
+    """One head repeated to the largest head count with paired waves (192 workgroups of 128
+    rows, 384 when causal) and to one more (one wave per 32 rows over all keys), at N = 100
+    and N = 128 (one tile)."""
+    limit = 384 if causal else 192
     for N in (100, 128):
         q, k, v = make_qkv(1, 1, N, 128, "bf16", seed=3100 + N)
-        for reps in (192, 193):
+        for reps in (limit, limit + 1):
             _check_repeated(fa, q, k, v, causal, reps, f"N={N} heads={reps} causal={causal}")
 
 

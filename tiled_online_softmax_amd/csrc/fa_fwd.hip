@@ -51,21 +51,25 @@ constexpr int kBf16Rows = kRowsPerWave * kBf16Waves;  // query rows per workgrou
 // Compute units of the MI355X (gfx950).
 constexpr int64_t kComputeUnits = 256;
 
-// Key split of the bf16 kernel for small grids: when one workgroup per 128
-// query rows would leave at least a quarter of the compute units idle, the
-// kernel runs with its waves paired over the key blocks of each tile (64 query
-// rows per workgroup, twice the workgroups, half the keys per wave).
+// Key split of the bf16 kernel for small grids: the kernel runs with its waves
+// paired over the key blocks of each tile (64 query rows per workgroup, twice
+// the workgroups, half the keys per wave) when one workgroup per 128 query rows
+// gives at most 3/4 of a workgroup per compute unit, or, when causal, at most
+// 3/2: causal workgroups differ in length (a query tile sees the keys up to
+// its diagonal), and while the grid fits in one round of two per compute unit
+// the longest one sets the time, which the split halves.
 constexpr int kBf16SmallGridSplit = 2;
-bool bf16_small_grid(int64_t BH, int64_t Nq) {
-  return 4 * BH * ((Nq + kBf16Rows - 1) / kBf16Rows) <= 3 * kComputeUnits;
+bool bf16_small_grid(int64_t BH, int64_t Nq, bool causal) {
+  const int64_t wgs = BH * ((Nq + kBf16Rows - 1) / kBf16Rows);
+  return causal ? 2 * wgs <= 3 * kComputeUnits : 4 * wgs <= 3 * kComputeUnits;
 }
-int64_t bf16_rows(int64_t BH, int64_t Nq) {
-  return bf16_small_grid(BH, Nq) ? kBf16Rows / kBf16SmallGridSplit : kBf16Rows;
+int64_t bf16_rows(int64_t BH, int64_t Nq, bool causal) {
+  return bf16_small_grid(BH, Nq, causal) ? kBf16Rows / kBf16SmallGridSplit : kBf16Rows;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bf16(int64_t BH, hipStream_t s, FwdParams p) {
-  if (bf16_small_grid(BH, p.Nq)) {
+  if (bf16_small_grid(BH, p.Nq, CAUSAL)) {
     constexpr int rows = kBf16Rows / kBf16SmallGridSplit;
     p.n_qtiles = (p.Nq + rows - 1) / rows;
     const void *kern = (const void *)&fa_fwd_bf16_kernel<D, CAUSAL, kBf16Waves, kBf16Keys, kBf16SmallGridSplit>;
@@ -236,15 +240,17 @@ FwdParams contiguous_params(const void *Q, const void *K, const void *V, void *O
 
 // Query rows per workgroup and threads per workgroup of the kernel that
 // launch_bf16 / launch_f32 pick for this shape.
-int64_t block_rows(int dtype, int64_t BH, int64_t N) { return dtype == FA_DTYPE_BF16 ? bf16_rows(BH, N) : kF32Rows; }
+int64_t block_rows(int dtype, int64_t BH, int64_t N, bool causal) {
+  return dtype == FA_DTYPE_BF16 ? bf16_rows(BH, N, causal) : kF32Rows;
+}
 int block_threads(int dtype) { return 64 * (dtype == FA_DTYPE_BF16 ? kBf16Waves : kF32Waves); }
 
 std::string kernel_expression(int dtype, int64_t d, int causal, int64_t BH, int64_t N) {
   const std::string c = causal ? "true" : "false";
   if (dtype == FA_DTYPE_BF16)
     return "fa_fwd_bf16_kernel<" + std::to_string(d) + ", " + c + ", " + std::to_string(kBf16Waves) + ", " +
-           std::to_string(kBf16Keys) + ", " + std::to_string(bf16_small_grid(BH, N) ? kBf16SmallGridSplit : 1) +
-           ">";
+           std::to_string(kBf16Keys) + ", " +
+           std::to_string(bf16_small_grid(BH, N, causal != 0) ? kBf16SmallGridSplit : 1) + ">";
   return "fa_fwd_f32_kernel<" + std::to_string(d) + ", " + c + ", " + std::to_string(kF32Waves) + ">";
 }
 
@@ -324,7 +330,7 @@ extern "C" fa_status_t fa_fwd_specialized(const void *Q, const void *K, const vo
     kern = it->second;
   }
   FwdParams p = contiguous_params(Q, K, V, O, L, H, N, d, scale);
-  const int64_t rows = block_rows(dtype, B * H, N);
+  const int64_t rows = block_rows(dtype, B * H, N, causal != 0);
   p.n_qtiles = (int)((N + rows - 1) / rows);
   void *args[] = {(void *)&p};
   const hipError_t err = hipModuleLaunchKernel(kern.function, (unsigned)(B * H * p.n_qtiles), 1, 1,
