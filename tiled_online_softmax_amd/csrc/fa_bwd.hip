@@ -60,6 +60,8 @@ __device__ __forceinline__ void load_lds_4(__amdgpu_buffer_rsrc_t rsrc, uint32_t
                :
                : "s"(lds), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
+#else
+  (void)rsrc, (void)lds, (void)voffset;
 #endif
 }
 

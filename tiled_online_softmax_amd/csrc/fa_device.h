@@ -147,6 +147,8 @@ __device__ __forceinline__ void load_lds_share(__amdgpu_buffer_rsrc_t rsrc, uint
                  :
                  : "s"(lds), "v"(vo[0]), "v"(vo[1]), "s"(rsrc)
                  : "memory", "m0");
+#else
+  (void)rsrc, (void)lds, (void)vo;
 #endif
 }
 

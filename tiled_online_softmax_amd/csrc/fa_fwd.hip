@@ -322,7 +322,7 @@ extern "C" fa_status_t fa_fwd_specialized(const void *Q, const void *K, const vo
       JitKernel k{};
       if (hipModuleLoadData(&k.module, code.data()) != hipSuccess) return FA_ERR_JIT;
       if (hipModuleGetFunction(&k.function, k.module, name.c_str()) != hipSuccess) {
-        hipModuleUnload(k.module);
+        (void)hipModuleUnload(k.module);  // already failing: the unload's status adds nothing
         return FA_ERR_JIT;
       }
       it = g_jit_kernels.emplace(key, k).first;
