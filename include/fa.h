@@ -28,7 +28,7 @@ extern "C" {
 /* Status codes. FA_OK is zero; every other value is an error. */
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, B/H/N < 1, scale not finite or <= 0, bad dtype */
+  FA_ERR_INVALID_ARGUMENT = 1, /* null pointer, B/H/N < 1, scale <= 0 or scale*log2(e) not finite in fp32, bad dtype */
   FA_ERR_UNSUPPORTED = 2,      /* head dimension not supported by the entry point, or a size too large */
   FA_ERR_MISALIGNED = 3,       /* a buffer not 16-byte aligned */
   FA_ERR_LAUNCH = 4,           /* the HIP runtime refused the kernel launch */
@@ -54,7 +54,7 @@ typedef enum {
  *            0..N-1). Each >= 1. N need not be a multiple of any tile size.
  *   d        head dimension: 16, 32, 64 or 128.
  *   causal   0: every query sees every key. Non-zero: query i sees keys j <= i.
- *   scale    multiplier of Q K^T (usually 1/sqrt(d)); finite and > 0.
+ *   scale    multiplier of Q K^T (usually 1/sqrt(d)); > 0, with scale * log2(e) finite in fp32.
  *   stream   hipStream_t to enqueue on (NULL = the null stream).
  *   dtype    an fa_dtype_t value.
  *

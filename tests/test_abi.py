@@ -55,8 +55,9 @@ def test_bad_sizes(kw):
     assert call(**kw) == fa.FA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan")])
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan"), 3.0e38])
 def test_bad_scale(scale):
+    """Non-positive or non-finite scales, and finite ones whose scale * log2(e) overflows fp32."""
     assert call(scale=scale) == fa.FA_ERR_INVALID_ARGUMENT
 
 
@@ -105,7 +106,7 @@ def test_bwd_null_pointer(name):
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(scale=0.0), dict(scale=float("nan")),
-                                dict(dtype=7)])
+                                dict(scale=3.0e38), dict(dtype=7)])
 def test_bwd_bad_arguments(kw):
     assert call_bwd(**kw) == fa.FA_ERR_INVALID_ARGUMENT
 
@@ -155,7 +156,8 @@ def test_strided_null(kw):
     assert call_strided(**kw) == fa.FA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("kw", [dict(Nq=0), dict(Nk=0), dict(B=0), dict(H=-1), dict(scale=0.0), dict(dtype=5)])
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(Nk=0), dict(B=0), dict(H=-1), dict(scale=0.0), dict(scale=3.0e38),
+                                dict(dtype=5)])
 def test_strided_bad_sizes(kw):
     assert call_strided(**kw) == fa.FA_ERR_INVALID_ARGUMENT
 

@@ -838,7 +838,8 @@ extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const
   if (!Q || !K || !V || !O || !L || !dO || !dQ || !dK || !dV || !work)
     return FA_ERR_INVALID_ARGUMENT;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARGUMENT;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !isfinite((float)((double)scale * 1.4426950408889634074)))  // finite scale * log2(e)
+    return FA_ERR_INVALID_ARGUMENT;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
   const bool bf = dtype == FA_DTYPE_BF16;
   // bf16: d = 64, 128 (the 8-wave dK/dV tile loads need 8 KiB tiles); fp32 also d = 32.

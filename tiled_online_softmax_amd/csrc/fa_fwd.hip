@@ -195,7 +195,7 @@ fa_status_t validate_contiguous(const void *Q, const void *K, const void *V, con
                                 int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype) {
   if (!Q || !K || !V || !O || !L) return FA_ERR_INVALID_ARGUMENT;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARGUMENT;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !isfinite(log2e_scale(scale))) return FA_ERR_INVALID_ARGUMENT;  // finite scale * log2(e)
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
   const size_t esize = dtype == FA_DTYPE_BF16 ? 2 : 4;
   if (!supported_head_dim(d)) return FA_ERR_UNSUPPORTED;
@@ -369,7 +369,7 @@ extern "C" fa_status_t fa_fwd_strided(const void *Q, const void *K, const void *
   if (!Q || !K || !V || !O || !L || !q_strides || !k_strides || !v_strides || !o_strides || !l_strides)
     return FA_ERR_INVALID_ARGUMENT;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARGUMENT;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !isfinite(log2e_scale(scale))) return FA_ERR_INVALID_ARGUMENT;  // finite scale * log2(e)
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARGUMENT;
   const int64_t *ts[4] = {q_strides, k_strides, v_strides, o_strides};
   for (const int64_t *st : ts)
