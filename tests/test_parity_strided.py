@@ -59,6 +59,25 @@ def test_cross_attention(fa, Nq, Nk, causal, d, dtype):
     _compare(O, L, Oref, Lref, dtype, f"{dtype} d={d} {Nq}x{Nk} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk", [(100, 300), (300, 100), (1, 257), (257, 1), (65, 65)])
+def test_cross_attention_large_grid_bf16(fa, Nq, Nk, causal, d):
+    """The bf16 kernel that gives each wave all keys of its 32 rows (grids above 192
+    workgroups of 128 rows, 384 when causal), through fa_fwd_strided with [B, N, H, d]
+    storage: two heads repeated to 400 in one launch, compared with the oracle on the
+    first two and bitwise among the repeats."""
+    q, k, v = make_qkv_cross(1, 2, Nq, Nk, d, "bf16", seed=5000 + Nq * 7 + Nk + d)
+    scale = default_scale(d)
+    Oref, Lref = _oracle_cross(q, k, v, causal, scale)
+    qd, kd, vd = (t.repeat(1, 200, 1, 1).transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v))
+    O, L = fa.forward_strided(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    _compare(O[:, :2], L[:, :2], Oref, Lref, "bf16", f"x200 bshd d={d} {Nq}x{Nk} causal={causal}")
+    for j in range(1, 200):
+        assert torch.equal(O[:, 2 * j:2 * j + 2], O[:, :2]) and torch.equal(L[:, 2 * j:2 * j + 2], L[:, :2])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [16, 32])
 @pytest.mark.parametrize("causal", [False, True])
