@@ -5,7 +5,12 @@ dK, dV. The outputs are rounded to bf16 (relative error <= 2^-9), and each produ
 term of the gradient carries one more bf16 rounding of P or dS as an MFMA operand
 (<= 2^-9 relative). The forward's O, rounded to bf16, enters D = sum_c dO O. A budget
 of five units of 2^-9 (~1e-2) of the largest entry covers these; the measured errors
-are 2.5e-3 to 5e-3 of it.
+are 2.5e-3 to 5e-3 of it at sigma 1. With wide logits (Q, K ~ N(0, 4^2)) and short rows
+the weights concentrate on a few keys, dP - D nearly cancels there, and the rounding of
+O inside D is amplified relative to the gradient: the random cases below reach 9.5e-3
+of the largest entry (dQ, d = 128, N = 32). Against an fp64 gradient that takes D from
+the same bf16 O the kernel's error on those cases is 2.4e-3 to 4.7e-3, so the rest is
+the method's use of the stored O, not the kernel's arithmetic.
 
 Tolerance (fp32): 2e-5 * max(1, max |dX_ref|). Every operand stays fp32, so the error
 comes from rounding: P = exp2(S c - L2) carries the forward's L error and the
@@ -160,3 +165,25 @@ def test_bwd_f32_wide_logits(fa, causal):
 def test_bwd_f32_other_scale(fa):
     q, k, v, do = _inputs(1, 2, 300, 64, seed=3000, dtype="f32")
     _check(fa, q, k, v, do, False, 0.3, "f32 scale 0.3")
+
+
+def _random_case(i):
+    r = np.random.RandomState(20261203 + i)
+    dtype = ("bf16", "f32")[r.randint(2)]
+    d = int((64, 128)[r.randint(2)]) if dtype == "bf16" else int((32, 64, 128)[r.randint(3)])
+    return dict(dtype=dtype, d=d, causal=bool(r.randint(2)), B=int(r.randint(1, 3)), H=int(r.randint(1, 4)),
+                N=int(r.choice([1, 5, 32, 33, 64, 96, 127, 130, 191, 256, 300])),
+                sigma=float((1.0, 2.0, 4.0)[r.randint(3)]), seed=8000 + i)
+
+
+RANDOM_CASES = [_random_case(i) for i in range(48)]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"c{i}" for i in range(len(RANDOM_CASES))])
+def test_bwd_random_configuration(fa, case):
+    """Seeded random (dtype, d, causal, B, H, N, logit width) through the forward and
+    backward entry points, against the fp64 gradient oracle."""
+    c = case
+    label = " ".join(f"{k}={v}" for k, v in c.items())
+    q, k, v, do = _inputs(c["B"], c["H"], c["N"], c["d"], c["seed"], sigma_qk=c["sigma"], dtype=c["dtype"])
+    _check(fa, q, k, v, do, c["causal"], default_scale(c["d"]), label)
