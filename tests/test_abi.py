@@ -233,3 +233,12 @@ def test_jit_code_object_arguments():
     assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 96, 0, 1, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_jit_code_object(7, 64, 0, 1, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_INVALID_ARGUMENT
     assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 64, 0, 0, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+def test_attention_checks_rank():
+    """The differentiable wrapper rejects tensors that are not [B, H, N, d] before any GPU call."""
+    import torch
+
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        fa.attention(x, x, x)

@@ -187,3 +187,36 @@ def test_bwd_random_configuration(fa, case):
     label = " ".join(f"{k}={v}" for k, v in c.items())
     q, k, v, do = _inputs(c["B"], c["H"], c["N"], c["d"], c["seed"], sigma_qk=c["sigma"], dtype=c["dtype"])
     _check(fa, q, k, v, do, c["causal"], default_scale(c["d"]), label)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_attention(fa, causal, dtype):
+    """fa.attention under torch.autograd: its output equals fa.forward's bitwise, and the
+    gradients of sum(O * dO), and of sum(O) (an expanded, stride-0 upstream gradient),
+    match the fp64 oracle's dQ, dK, dV."""
+    q, k, v, do = _inputs(2, 2, 200, 64, seed=2600 + causal, dtype=dtype)
+    scale = default_scale(64)
+    dev = torch.device("cuda:0")
+    tol = TOL["f32" if dtype == "f32" else "bf16"]
+    for upstream in ("dO", "ones"):
+        qd, kd, vd = (t.to(dev).requires_grad_() for t in (q, k, v))
+        out = fa.attention(qd, kd, vd, causal=causal)
+        O2, _ = fa.forward(qd.detach(), kd.detach(), vd.detach(), causal=causal, scale=scale)
+        assert torch.equal(out.detach(), O2)
+        if upstream == "dO":
+            out.backward(do.to(dev))
+            g = do
+        else:
+            out.sum().backward()
+            g = torch.ones_like(do)
+        torch.cuda.synchronize()
+        ref = oracle.attention_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                   g.double().numpy(), causal, scale)
+        for name, t, r in zip(("dQ", "dK", "dV"), (qd, kd, vd), ref):
+            a = t.grad.double().cpu().numpy()
+            err = float(np.abs(a - r).max())
+            bound = tol * max(1.0, float(np.abs(r).max()))
+            print(f"[autograd] {dtype} causal={causal} {upstream} {name} max|err|={err:.3e} (tol {bound:.3e})",
+                  flush=True)
+            assert err <= bound, f"{name}: {err} > {bound}"

@@ -2,7 +2,8 @@
 
 ``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_specialized`` and ``fa_bwd`` mirror the C
 entry points of ``libfa.so``; ``forward``, ``forward_strided``, ``forward_specialized``
-and ``backward`` allocate the outputs (and the backward workspace) and call them.
+and ``backward`` allocate the outputs (and the backward workspace) and call them;
+``attention`` is the differentiable form (fa_fwd forward, fa_bwd backward).
 Importing fails loudly when the HIP library is not built.
 """
 
@@ -17,6 +18,7 @@ from ._binding import (  # noqa: F401
     FA_OK,
     LIB_PATH,
     FaError,
+    attention,
     backward,
     fa_bwd,
     fa_fwd,

@@ -289,3 +289,32 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     work = torch.empty(2 * B * H * N, dtype=torch.float32, device=q.device)
     fa_bwd(q, k, v, o, lse, do, dq, dk, dv, work, B, H, N, d, causal, scale, stream)
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """fa_fwd in the forward pass (O and L kept), fa_bwd in the backward pass."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = forward(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """O = softmax(scale q k^T) v (optionally causal) for contiguous [B, H, N, d] device
+    tensors, differentiable: the gradient runs fa_bwd on the saved O and L. The forward
+    pass takes d in {16, 32, 64, 128}; the backward pass d in {64, 128} (fp32 also 32)
+    and raises FaError otherwise. ``scale`` defaults to 1/sqrt(d) rounded to fp32."""
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    if scale is None:
+        scale = float(torch.tensor(q.shape[-1] ** -0.5, dtype=torch.float32).item())
+    return _Attention.apply(q, k, v, bool(causal), float(scale))
