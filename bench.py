@@ -10,7 +10,8 @@ The roofline object compares the kernel against the MI355X published dense bf16
 MFMA peak; ``traffic`` is the HBM traffic measured by rocprofv3 counters for the
 same kernel source (null when the kernel source has changed since). The CPU
 baseline times the fp64 oracle on a bounded sample of query rows on the host cores
-(on the GPU machine), and checks the sampled rows of the GPU output against it.
+of the machine that runs the benchmark, and checks the sampled rows of the GPU output
+against it.
 
 ``--pass bwd`` times the backward pass instead (one fa_bwd call: the preprocessing,
 dQ and dK/dV kernels) on the same workload with a seeded dO, with algorithmic
