@@ -265,6 +265,8 @@ def main():
                     help="untimed launches first: the GPU clock ramps up under sustained load")
     ap.add_argument("--workload", default=None, help="workload name (default: the causal bf16 B4 H16 N4096 d128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8, metavar="K",
+                    help="record a HIP event pair around every K-th timed launch (per-launch kernel time)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward pass")
@@ -344,18 +346,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: HIP events on the stream the kernel is enqueued on.
+    # Timed region: HIP events on the stream the kernel is enqueued on, around the whole
+    # region and around every `event_every`-th launch (the per-launch event pairs add a
+    # few microseconds between launches, so the others run back to back).
+    every = max(1, args.event_every)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(0, args.steps, every)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for (a, b) in per:
-        a.record(stream)
-        step()
-        b.record(stream)
+    for i in range(args.steps):
+        if i % every == 0:
+            a, b = per[i // every]
+            a.record(stream)
+            step()
+            b.record(stream)
+        else:
+            step()
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -398,7 +407,8 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_ms": {"avg": round(avg_launch_ms, 5), "median": round(launch_ms[len(launch_ms) // 2], 5),
-                          "min": round(launch_ms[0], 5), "max": round(launch_ms[-1], 5)},
+                          "min": round(launch_ms[0], 5), "max": round(launch_ms[-1], 5),
+                          "launches_timed": len(launch_ms)},
             "algorithmic_flop_per_launch": flops,
             "algorithmic_bytes_per_launch": io_bytes,
         },
