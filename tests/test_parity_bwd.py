@@ -1,16 +1,22 @@
 """GPU parity of the backward pass (fa_bwd through the C ABI) against the fp64 oracle.
 
 Tolerance (bf16): max |dX_gpu - dX_ref| <= 1e-2 * max(1, max |dX_ref|) for each of dQ,
-dK, dV. The outputs are rounded to bf16 (relative error <= 2^-9), and each product
+dK, dV. The outputs are rounded to bf16 (unit roundoff u = 2^-8), and each product
 term of the gradient carries one more bf16 rounding of P or dS as an MFMA operand
-(<= 2^-9 relative). The forward's O, rounded to bf16, enters D = sum_c dO O. A budget
-of five units of 2^-9 (~1e-2) of the largest entry covers these; the measured errors
-are 2.5e-3 to 5e-3 of it at sigma 1. With wide logits (Q, K ~ N(0, 4^2)) and short rows
-the weights concentrate on a few keys, dP - D nearly cancels there, and the rounding of
-O inside D is amplified relative to the gradient: the random cases below reach 9.5e-3
-of the largest entry (dQ, d = 128, N = 32). Against an fp64 gradient that takes D from
-the same bf16 O the kernel's error on those cases is 2.4e-3 to 4.7e-3, so the rest is
-the method's use of the stored O, not the kernel's arithmetic.
+(<= u relative). The forward's O, rounded to bf16, enters D = sum_c dO O. A budget of
+2.5 u (~1e-2) of the largest entry covers these for the cases below; their measured
+errors are 2.5e-3 to 5e-3 of it at sigma 1 and up to 9.5e-3 with wide logits.
+
+The budget is not a bound for every input. With wide logits (Q, K ~ N(0, 2^2) or
+N(0, 4^2)) and short rows the weights concentrate on a few keys, dP - D nearly cancels
+there, and the error of the stored O inside D is amplified relative to the gradient.
+A sweep of 1000 seeded random cases (FA_RANDOM_BWD_CASES=1000) met 15 bf16 cases above
+the budget, by up to 4.5x (dQ, N = 5, d = 128, sigma 4). Against an fp64 gradient that
+takes D from the same bf16 O as the kernels, all 15 stay at 1.7e-3 to 5.1e-3 of the
+largest entry: the excess is the method's D from the stored bf16 O, not the kernels'
+arithmetic. A rigorous bound on that term (the rounding of O propagated through
+dS = P (dP - D) with absolute values) is 4 to 10 times looser than what those cases
+need, so the tests keep the budget and their fixed seeds.
 
 Tolerance (fp32): 2e-5 * max(1, max |dX_ref|). Every operand stays fp32, so the error
 comes from rounding: P = exp2(S c - L2) carries the forward's L error and the
@@ -20,6 +26,8 @@ sums up to N such terms in fp32 (random-walk growth ~sqrt(N) 2^-24). The measure
 errors are 2e-7 to 2e-6 of the largest entry at sigma 1 (N up to 4100) and up to
 7.4e-6 at sigma 4, where |S c| is largest.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -176,7 +184,8 @@ def _random_case(i):
                 sigma=float((1.0, 2.0, 4.0)[r.randint(3)]), seed=8000 + i)
 
 
-RANDOM_CASES = [_random_case(i) for i in range(48)]
+# FA_RANDOM_BWD_CASES raises the count for a longer sweep (the same seeds first).
+RANDOM_CASES = [_random_case(i) for i in range(int(os.environ.get("FA_RANDOM_BWD_CASES", "48")))]
 
 
 @pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"c{i}" for i in range(len(RANDOM_CASES))])
