@@ -66,7 +66,11 @@ typedef enum {
  * nothing is enqueued and O, L are untouched. Faults inside the kernel (for
  * example a pointer that is not device memory) surface at the caller's next
  * synchronisation, not here. Calls on different streams may run
- * concurrently; they share no state.
+ * concurrently; they share no state. Repeated calls with the same arguments
+ * and data give bitwise identical results; with bf16, a head's result can
+ * differ in the last bits between launches with different B, H or N, because
+ * small grids split each tile's keys between two waves (a different
+ * summation order, within the same error bound).
  */
 fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void *O, float *L,
                    int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
