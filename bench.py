@@ -238,6 +238,18 @@ def small_sweep(reps: int):
         O = torch.empty_like(q)
         L = torch.empty((1, 1, w.N), dtype=torch.float32, device=dev)
         ours = timed(lambda: fa.fa_fwd(q, k, v, O, L, 1, 1, w.N, w.d, w.causal, w.scale, stream))
+        # The same call captured once into a HIP graph and replayed (no Python or
+        # argument checks per launch).
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fa.fa_fwd(q, k, v, O, L, 1, 1, w.N, w.d, w.causal, w.scale)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fa.fa_fwd(q, k, v, O, L, 1, 1, w.N, w.d, w.causal, w.scale)
+        replay = timed(graph.replay)
         sdpa = timed(lambda: F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale))
         expl = timed(lambda: explicit(q, k, v, w.causal, w.scale))
         ref = F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
@@ -245,6 +257,7 @@ def small_sweep(reps: int):
         rec = {"sweep": "small_shapes_f32", "workload": w.name, "N": w.N, "d": w.d, "causal": w.causal,
                "fa_fwd_us": round(ours[0], 2), "sdpa_us": round(sdpa[0], 2), "explicit_us": round(expl[0], 2),
                "fa_fwd_host_us": round(ours[1], 2), "sdpa_host_us": round(sdpa[1], 2),
+               "fa_fwd_graph_replay_us": round(replay[0], 2), "fa_fwd_graph_replay_host_us": round(replay[1], 2),
                "explicit_host_us": round(expl[1], 2),
                "max_abs_diff_vs_sdpa": float((O - ref).abs().max()), "reps": reps}
         rows.append(rec)
