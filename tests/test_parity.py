@@ -167,6 +167,17 @@ def test_bf16_grid_size_threshold(fa, causal):
             _check_repeated(fa, q, k, v, causal, reps, f"N={N} heads={reps} causal={causal}")
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 16, 2048, 128, True), (1, 24, 2048, 64, True),
+                                             (1, 8, 2048, 128, False), (1, 32, 2048, 128, True)])
+def test_bf16_long_rows_both_forms(fa, B, H, N, d, causal):
+    """Long rows on either side of the key-split switch (causal: 256 and 384 workgroups of
+    128 rows use the split, 512 do not; non-causal: 128 use it), compared on 24 sampled
+    query rows of every head."""
+    q, k, v = make_qkv(B, H, N, d, "bf16", seed=3200 + H + d)
+    rows = sample_rows(N, 24, seed=3200 + H)
+    _check(fa, q, k, v, causal, default_scale(d), "bf16", rows=rows, label=f"B{B} H{H} N{N} d{d} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_grid_not_multiple_of_xcds(fa, causal):
     """B*H*tiles = 3*37*2 = 222 workgroups: the XCD renumbering must stay a bijection."""
