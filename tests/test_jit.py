@@ -44,3 +44,15 @@ def test_shapes_give_different_code(tmp_path):
     a = fa.jit_code_object(fa.FA_DTYPE_BF16, 64, False, 1, 2, 1000)
     b = fa.jit_code_object(fa.FA_DTYPE_BF16, 64, False, 1, 2, 1024)
     assert a != b
+
+
+@pytest.mark.parametrize("causal,heads,split", [(False, 192, True), (False, 193, False),
+                                                (True, 384, True), (True, 385, False)])
+def test_key_split_selection(causal, heads, split):
+    """The bf16 forward compiles the key-split form (template argument KS = 2) exactly when
+    B*H*ceil(N/128) is at most 192 workgroups, or 384 when causal; fa_fwd_specialized and
+    fa_fwd make the same choice. The kernel symbol in the code object names the form."""
+    co = fa.jit_code_object(fa.FA_DTYPE_BF16, 128, causal, 1, heads, 128)
+    ks = re.findall(rb"fa_fwd_bf16_kernelILi128ELb[01]ELi4ELi64ELi([12])E", co)
+    assert ks, "bf16 kernel symbol not found in the code object"
+    assert set(ks) == {b"2" if split else b"1"}
