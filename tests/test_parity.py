@@ -1,9 +1,10 @@
 """HIP path vs the fp64 oracle, element by element (needs an MI355X).
 
 Tolerances (max abs error): O 1e-5 / L 1e-4 for fp32, O 2e-2 / L 1e-2 for bf16.
-Small workloads are compared in full; the two large causal workloads run at full
-size in the launch configuration the benchmark times and are compared on sampled
-query rows of every head, plus properties that hold at every row.
+Every workload is compared with the oracle on every row of every head; the two large
+causal workloads run at full size in the launch configuration the benchmark times (the
+oracle evaluates them head by head), and their outputs are also checked for properties
+that hold at every row.
 """
 
 import math
@@ -13,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import WORKLOADS, default_scale, make_qkv, sample_rows
+from workloads import WORKLOADS, default_scale, make_qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -80,15 +81,37 @@ def _convex_hull_check(O, v, causal):
     assert bool(((Of >= lo - slack) & (Of <= hi + slack)).all()), "output outside the value hull"
 
 
+def _errors_by_head(O, L, q, k, v, causal, scale, label):
+    """Max |O - O_ref| and |L - L_ref| over every row of every head, the oracle run one
+    head at a time (its S and P for one head are N x N fp64)."""
+    o = O.double().cpu().numpy()
+    lse = L.double().cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "non-finite output"
+    qn, kn, vn = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    B, H = q.shape[0], q.shape[1]
+    eo = el = 0.0
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            Oref, Lref = oracle.attention(qn[sl], kn[sl], vn[sl], causal, scale)
+            eo = max(eo, float(np.max(np.abs(o[sl] - Oref))))
+            el = max(el, float(np.max(np.abs(lse[sl] - Lref))))
+        print(f"[parity] {label} heads {(b + 1) * H}/{B * H} max|dO|={eo:.3e} max|dL|={el:.3e}", flush=True)
+    return eo, el
+
+
 @pytest.mark.parametrize("name", ["causal_bf16_b4h16n4096d128", "long_causal_bf16_h32n16384d64"])
-def test_workload_full_size_sampled(fa, name):
+def test_workload_full_size_every_row(fa, name):
     w = WORKLOADS[name]
     q, k, v = w.make()
-    rows = sample_rows(w.N, 24, seed=w.seed)
-    O, L = _check(fa, q, k, v, w.causal, w.scale, w.dtype, rows=rows, label=f"{name} rows={len(rows)}")
-    # Every row, at full size: finite, inside the value hull, and L >= the diagonal score
-    # (the diagonal key is always admissible) and <= max score + log(#admissible keys).
-    assert bool(torch.isfinite(O.float()).all()) and bool(torch.isfinite(L).all())
+    O, L = _run(fa, q, k, v, w.causal, w.scale)
+    eo, el = _errors_by_head(O, L, q, k, v, w.causal, w.scale, name)
+    otol, ltol = TOL[w.dtype]
+    print(f"[parity] {name} every row: max|dO|={eo:.3e} (tol {otol}) max|dL|={el:.3e} (tol {ltol})", flush=True)
+    assert eo <= otol, f"{name}: O error {eo} > {otol}"
+    assert el <= ltol, f"{name}: L error {el} > {ltol}"
+    # Properties of every row: inside the value hull, and L >= the diagonal score (the
+    # diagonal key is always admissible) and <= max score + log(#admissible keys).
     _convex_hull_check(O, v, w.causal)
     qd, kd = q.to(O.device).float(), k.to(O.device).float()
     diag = (qd * kd).sum(-1) * w.scale
@@ -100,12 +123,11 @@ def test_workload_full_size_sampled(fa, name):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
-def test_f32_long_sampled(fa, causal, d):
+def test_f32_long(fa, causal, d):
     """fp32 at N = 4100: 129 key tiles spread over the waves of a workgroup (uneven
-    shares, a ragged last tile), checked on sampled rows."""
+    shares, a ragged last tile), every row."""
     q, k, v = make_qkv(2, 4, 4100, d, "f32", seed=51 + d)
-    rows = sample_rows(4100, 24, seed=52)
-    _check(fa, q, k, v, causal, default_scale(d), "f32", rows=rows, label=f"fp32 N=4100 d={d} causal={causal}")
+    _check(fa, q, k, v, causal, default_scale(d), "f32", label=f"fp32 N=4100 d={d} causal={causal}")
 
 
 EDGE_N = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 1000]
@@ -171,11 +193,12 @@ def test_bf16_grid_size_threshold(fa, causal):
                                              (1, 8, 2048, 128, False), (1, 32, 2048, 128, True)])
 def test_bf16_long_rows_both_forms(fa, B, H, N, d, causal):
     """Long rows on either side of the key-split switch (causal: 256 and 384 workgroups of
-    128 rows use the split, 512 do not; non-causal: 128 use it), compared on 24 sampled
-    query rows of every head."""
+    128 rows use the split, 512 do not; non-causal: 128 use it), every row of every head."""
     q, k, v = make_qkv(B, H, N, d, "bf16", seed=3200 + H + d)
-    rows = sample_rows(N, 24, seed=3200 + H)
-    _check(fa, q, k, v, causal, default_scale(d), "bf16", rows=rows, label=f"B{B} H{H} N{N} d{d} causal={causal}")
+    O, L = _run(fa, q, k, v, causal, default_scale(d))
+    label = f"B{B} H{H} N{N} d{d} causal={causal}"
+    eo, el = _errors_by_head(O, L, q, k, v, causal, default_scale(d), label)
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1], f"{label}: O error {eo}, L error {el}"
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -262,7 +285,9 @@ def test_bf16_close_to_fp32(fa):
     Ob, Lb = _run(fa, q, k, v, True, default_scale(64))
     Of, Lf = _run(fa, q.float(), k.float(), v.float(), True, default_scale(64))
     assert float((Ob.float() - Of).abs().max()) <= 2e-2
-    assert float((Lb - Lf).abs().max()) <= 1e-3
+    # The bf16 kernel's row sum adds the bf16-rounded weights (relative error <= u = 2^-8
+    # each), so its L may differ by up to log(1 + 2^-8) = 3.9e-3 from the fp32 sum.
+    assert float((Lb - Lf).abs().max()) <= 4e-3
 
 
 def test_errors_raise(fa):

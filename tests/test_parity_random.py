@@ -44,8 +44,14 @@ def _case(i):
                 reps=reps, seed=7000 + i)
 
 
-# FA_RANDOM_CASES raises the count for a longer sweep (the same seeds first).
-CASES = [_case(i) for i in range(int(os.environ.get("FA_RANDOM_CASES", "96")))]
+# FA_RANDOM_CASES raises the count for a longer sweep (the same seeds first). The fixed
+# extra cases are the four bf16 ones (sigma 4 logits, one dominant key with a large value)
+# that a 10000-case sweep found above the O tolerance when the row sum added the fp32
+# weights instead of the bf16 weights that enter the second product.
+_REGRESSION = (301, 1074, 8125, 9886)
+_N_RANDOM = int(os.environ.get("FA_RANDOM_CASES", "96"))
+CASE_IDS = list(range(_N_RANDOM)) + [i for i in _REGRESSION if i >= _N_RANDOM]
+CASES = [_case(i) for i in CASE_IDS]
 
 
 def _store(t, layout):
@@ -67,7 +73,7 @@ def fa():
     return tiled_online_softmax_amd
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in CASE_IDS])
 def test_random_configuration(fa, case):
     c = case
     label = " ".join(f"{k}={v}" for k, v in c.items())

@@ -323,13 +323,23 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
 #pragma unroll
         for (int t8 = 0; t8 < 8; ++t8) pb[kb][mm][t8] = (bf16)s[kb][8 * mm + t8];
   };
-  auto rowsum = [&](const f32x16 (&s)[NKW]) {
-    float ps = 0.f;
+  // Adds to `acc` the row sum of the weights as they enter the second MFMA: the
+  // bf16 values of P, two per v_dot2_f32_bf16 against (1, 1). Dividing by this
+  // sum makes each output row an exact convex combination of the value rows
+  // under the rounded weights (the rounding of a weight then cancels between
+  // numerator and denominator when one key dominates a row).
+  auto rowsum_into = [&](const bf16x8 (&pb)[NKW][2], float acc) {
+    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
     for (int kb = 0; kb < NKW; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ps += s[kb][r];
-    return ps;
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x2 w = {pb[kb][mm][2 * i], pb[kb][mm][2 * i + 1]};
+          acc = __builtin_amdgcn_fdot2_f32_bf16(w, one, acc, false);
+        }
+    return acc;
   };
   // O^T += V^T P^T for tile t. The A operand (V^T) lists the keys of P's slots
   // 16mm + 8(t/4) + 4hh + t%4 via two transposing reads of 4 consecutive keys.
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
     scores(t + 1, s_nxt, std::false_type{});
     exponentiate(s_cur, pb);
     accumulate(t, pb, std::false_type{});
-    lsum += rowsum(s_cur);
+    lsum = rowsum_into(pb, lsum);
     update_ref(rowmax(s_nxt));
   };
   auto iteration_edge = [&](int t, f32x16 (&s_cur)[NKW], f32x16 (&s_nxt)[NKW]) {
@@ -385,7 +395,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
     if (has_next) scores(t + 1, s_nxt, std::true_type{});
     exponentiate(s_cur, pb);
     accumulate(t, pb, std::true_type{});
-    lsum += rowsum(s_cur);
+    lsum = rowsum_into(pb, lsum);
     if (has_next) {
       if (t + 1 >= nfull) mask(t + 1, s_nxt);
       update_ref(rowmax(s_nxt));
