@@ -59,3 +59,37 @@ def test_backward_pins_catch_planted_mistake(name, tmp_path):
         except (AssertionError, RuntimeError):
             caught.append(pin.__name__)
     assert caught, f"planted mistake {name!r} passed every pin"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 5, 17])
+def test_stored_statistics_gradient_identity(N, causal):
+    """The GPU tests' reference for a backward that reads a stored O and L: its closed form
+    (oracle calls with rescaled upstream gradients) equals the backward's formulas
+    evaluated directly on a perturbed O and L -- P = exp(S - L'), D = sum_c dO O',
+    dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO -- in fp64."""
+    import torch
+
+    from bwd_reference import stored_statistics_gradient
+
+    rng = np.random.RandomState(40 + N + 100 * causal)
+    B, H, d, scale = 1, 2, 6, 0.7
+    q, k, v, do = (rng.standard_normal((B, H, N, d)) * s for s in (1.5, 1.5, 1.0, 1.0))
+    O, L = oracle.attention(q, k, v, causal, scale)
+    O2 = O + 1e-2 * rng.standard_normal(O.shape)
+    L2 = L + 1e-2 * rng.standard_normal(L.shape)
+    ref, stored = stored_statistics_gradient(*(torch.from_numpy(x) for x in (q, k, v, do)),
+                                             torch.from_numpy(O2), torch.from_numpy(L2), causal, scale)
+    for b in range(B):
+        for h in range(H):
+            S = scale * q[b, h] @ k[b, h].T
+            if causal:
+                S = np.where(np.tril(np.ones((N, N), dtype=bool)), S, -np.inf)
+            P = np.exp(S - L2[b, h][:, None])
+            D = np.sum(do[b, h] * O2[b, h], axis=-1)
+            dS = P * (do[b, h] @ v[b, h].T - D[:, None])
+            direct = (scale * dS @ k[b, h], scale * dS.T @ q[b, h], P.T @ do[b, h])
+            for name, x, y, r in zip(("dQ", "dK", "dV"), stored, direct, ref):
+                assert np.allclose(x[b, h], y, rtol=0, atol=1e-12), name
+                if N > 1:  # the perturbation is visible in every gradient
+                    assert np.abs(x[b, h] - r[b, h]).max() > 1e-6, name

@@ -1,30 +1,46 @@
 """GPU parity of the backward pass (fa_bwd through the C ABI) against the fp64 oracle.
 
-Tolerance (bf16): max |dX_gpu - dX_ref| <= 1e-2 * max(1, max |dX_ref|) for each of dQ,
-dK, dV. The outputs are rounded to bf16 (unit roundoff u = 2^-8), and each product
-term of the gradient carries one more bf16 rounding of P or dS as an MFMA operand
-(<= u relative). The forward's O, rounded to bf16, enters D = sum_c dO O. A budget of
-2.5 u (~1e-2) of the largest entry covers these for the cases below; their measured
-errors are 2.5e-3 to 5e-3 of it at sigma 1 and up to 9.5e-3 with wide logits.
+What the backward computes from its inputs. The method recomputes the weights from the
+stored logsumexp, P = exp(S - L), and takes D = sum_c dO O from the stored output
+("FlashAttention-2 from PyTorch to Triton", section "What We Are Building"; the forward's
+L and O are inputs of the backward). The stored O and L carry the forward's roundings,
+so the exact gradient of the function differs from the exact result of the method's
+formulas evaluated on the stored statistics. That difference is known in closed form:
+with lambda_i = L_stored_i - L_i and dD_i = sum_c dO_ic (O_stored_ic - O_ic),
 
-The budget is not a bound for every input. With wide logits (Q, K ~ N(0, 2^2) or
-N(0, 4^2)) and short rows the weights concentrate on a few keys, dP - D nearly cancels
-there, and the error of the stored O inside D is amplified relative to the gradient.
-A sweep of 1000 seeded random cases (FA_RANDOM_BWD_CASES=1000) met 15 bf16 cases above
-the budget, by up to 4.5x (dQ, N = 5, d = 128, sigma 4). Against an fp64 gradient that
-takes D from the same bf16 O as the kernels, all 15 stay at 1.7e-3 to 5.1e-3 of the
-largest entry: the excess is the method's D from the stored bf16 O, not the kernels'
-arithmetic. A rigorous bound on that term (the rounding of O propagated through
-dS = P (dP - D) with absolute values) is 4 to 10 times looser than what those cases
-need, so the tests keep the budget and their fixed seeds.
+    P'  = P exp(-lambda)            (per row)
+    dS' = P' (dP - D - dD)          = exp(-lambda) dS - exp(-lambda) dD P
+    dV' = P'^T dO                   = dV + dV[alpha dO]
+    dQ' = scale dS' K               = dQ + dQ[alpha dO] - scale beta (P K)
+    dK' = scale dS'^T Q             = dK + dK[alpha dO] - scale (P^T (beta Q))
 
-Tolerance (fp32): 2e-5 * max(1, max |dX_ref|). Every operand stays fp32, so the error
-comes from rounding: P = exp2(S c - L2) carries the forward's L error and the
-exponent's rounding (|S c| up to ~30 at sigma 4, so ~30 * 2^-24 ~ 2e-6 relative),
-dP - D cancels two sums of d products, each of size up to ~sqrt(d), and each gradient
-sums up to N such terms in fp32 (random-walk growth ~sqrt(N) 2^-24). The measured
-errors are 2e-7 to 2e-6 of the largest entry at sigma 1 (N up to 4100) and up to
-7.4e-6 at sigma 4, where |S c| is largest.
+where alpha_i = exp(-lambda_i) - 1, beta_i = exp(-lambda_i) dD_i, and X[g] is the exact
+gradient for the upstream gradient g (the gradient is linear in the rows of dO). Every
+term is an oracle call: the backward oracle with dO replaced by alpha dO or by beta Q
+(its dV is then P^T (beta Q)), and the forward oracle with V replaced by K (P K).
+
+Tolerance. bf16: max |dX_gpu - dX'| <= tol * max(1, max |dX_ref|) per tensor, with dX'
+the stored-statistics gradient above, so the error against the exact gradient is bounded
+by that budget plus max |dX' - dX_ref|, the exact effect of the stored O and L (their
+deviations come from O's rounding to bf16 and the rounded weights summed into l, which
+the backward does not reproduce). fp32: max |dX_gpu - dX_ref| <= tol * max(1, max
+|dX_ref|) against the exact gradient: the stored L deviates only through the fp32
+rounding of the scores, which the backward reproduces when it recomputes them, so the
+deviation cancels instead of propagating (correcting for it overshoots: a 1000-case
+sweep put fp32 errors against dX' at up to twice those against dX_ref).
+  * bf16, tol = 1e-2: the outputs are rounded to bf16 (unit roundoff u = 2^-8), and each
+    product term carries one more bf16 rounding of P or dS as an MFMA operand (<= u
+    relative); 2.5 u of the largest entry covers both. Measured: 2.5e-3 to 5e-3 of it at
+    sigma 1 and up to 9.5e-3 with wide logits. Before the stored-statistics term was
+    separated, a 1000-case random sweep met 15 bf16 cases where D's use of the stored O
+    exceeded the budget alone, by up to 4.5x (dQ, N = 5, d = 128, sigma 4); they are
+    kept below as fixed cases.
+  * fp32, tol = 2e-5: every operand stays fp32, so the error comes from rounding:
+    P = exp2(S c - L2) carries the exponent's rounding (|S c| up to ~30 at sigma 4, so
+    ~30 * 2^-24 ~ 2e-6 relative), dP - D cancels two sums of d products, each of size up
+    to ~sqrt(d), and each gradient sums up to N such terms in fp32 (random-walk growth
+    ~sqrt(N) 2^-24). The measured errors are 2e-7 to 2e-6 of the largest entry at
+    sigma 1 (N up to 4100) and up to 7.4e-6 at sigma 4, where |S c| is largest.
 """
 
 import os
@@ -34,6 +50,7 @@ import pytest
 import torch
 
 import oracle
+from bwd_reference import stored_statistics_gradient
 from workloads import default_scale, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -57,25 +74,34 @@ def _inputs(B, H, N, d, seed, sigma_qk=1.0, dtype="bf16"):
 
 
 def _run(fa, q, k, v, do, causal, scale):
+    """Forward then backward on the GPU: (dQ, dK, dV) and the stored (O, L)."""
     dev = torch.device("cuda:0")
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
     O, L = fa.forward(qd, kd, vd, causal=causal, scale=scale)
     dq, dk, dv = fa.backward(qd, kd, vd, O, L, dod, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    return dq, dk, dv
+    return (dq, dk, dv), (O, L)
 
 
 def _check(fa, q, k, v, do, causal, scale, label):
-    got = _run(fa, q, k, v, do, causal, scale)
-    ref = oracle.attention_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(),
-                               do.double().numpy(), causal, scale)
-    tol = TOL["f32" if q.dtype == torch.float32 else "bf16"]
-    for name, a, r in zip(("dQ", "dK", "dV"), got, ref):
+    got, (O, L) = _run(fa, q, k, v, do, causal, scale)
+    ref, stored = stored_statistics_gradient(q, k, v, do, O, L, causal, scale)
+    f32 = q.dtype == torch.float32
+    tol = TOL["f32" if f32 else "bf16"]
+    # fp32: the stored L deviates only through the fp32 rounding of the scores, which the
+    # backward reproduces when it recomputes them, so the two cancel and the reference is
+    # the exact gradient. bf16: the deviations come from O's rounding to bf16 and the
+    # rounded weights summed into l, which the backward does not reproduce.
+    target = ref if f32 else stored
+    for name, a, r, s in zip(("dQ", "dK", "dV"), got, ref, target):
         a = a.double().cpu().numpy()
         assert np.isfinite(a).all(), f"{label}: {name} not finite"
-        err = float(np.abs(a - r).max())
+        err_exact = float(np.abs(a - r).max())
+        err = float(np.abs(a - s).max())
+        stat = float(np.abs(s - r).max())
         bound = tol * max(1.0, float(np.abs(r).max()))
-        print(f"[parity-bwd] {label} {name} max|err|={err:.3e} (tol {bound:.3e})", flush=True)
+        print(f"[parity-bwd] {label} {name} max|err|={err:.3e} (tol {bound:.3e}) vs exact {err_exact:.3e} "
+              f"(<= tol + stored O, L effect {stat:.3e})", flush=True)
         assert err <= bound, f"{label}: {name} error {err} > {bound}"
 
 
@@ -121,9 +147,9 @@ def test_bwd_other_scale(fa):
 def test_bwd_deterministic(fa, dtype):
     """Every output element is reduced in a fixed order: repeated launches are bitwise identical."""
     q, k, v, do = _inputs(2, 4, 777, 128, seed=2500, dtype=dtype)
-    a = _run(fa, q, k, v, do, True, default_scale(128))
+    a, _ = _run(fa, q, k, v, do, True, default_scale(128))
     for _ in range(3):
-        b = _run(fa, q, k, v, do, True, default_scale(128))
+        b, _ = _run(fa, q, k, v, do, True, default_scale(128))
         for x, y in zip(a, b):
             assert torch.equal(x, y)
 
@@ -184,11 +210,16 @@ def _random_case(i):
                 sigma=float((1.0, 2.0, 4.0)[r.randint(3)]), seed=8000 + i)
 
 
-# FA_RANDOM_BWD_CASES raises the count for a longer sweep (the same seeds first).
-RANDOM_CASES = [_random_case(i) for i in range(int(os.environ.get("FA_RANDOM_BWD_CASES", "48")))]
+# FA_RANDOM_BWD_CASES raises the count for a longer sweep (the same seeds first). The
+# fixed extra cases are the 15 of a 1000-case sweep whose error against the exact
+# gradient passed the budget alone (wide logits, short rows: D's use of the stored O).
+_BWD_REGRESSION = (63, 102, 106, 233, 289, 306, 337, 454, 469, 605, 612, 881, 917, 947, 949)
+_N_RANDOM_BWD = int(os.environ.get("FA_RANDOM_BWD_CASES", "48"))
+RANDOM_CASE_IDS = list(range(_N_RANDOM_BWD)) + [i for i in _BWD_REGRESSION if i >= _N_RANDOM_BWD]
+RANDOM_CASES = [_random_case(i) for i in RANDOM_CASE_IDS]
 
 
-@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"c{i}" for i in range(len(RANDOM_CASES))])
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"c{i}" for i in RANDOM_CASE_IDS])
 def test_bwd_random_configuration(fa, case):
     """Seeded random (dtype, d, causal, B, H, N, logit width) through the forward and
     backward entry points, against the fp64 gradient oracle."""
