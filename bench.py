@@ -275,7 +275,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=500,
-                    help="untimed launches first: the GPU clock ramps up under sustained load")
+                    help="untimed launches before the timed region (after the clock warm-up)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0, metavar="S",
+                    help="first keep launching untimed steps for S seconds of wall time: the GPU "
+                         "clock ramps up over the first tens of milliseconds of sustained load, so "
+                         "a short --warmup alone leaves it ramping inside the timed region")
     ap.add_argument("--workload", default=None, help="workload name (default: the causal bf16 B4 H16 N4096 d128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=8, metavar="K",
@@ -355,6 +359,16 @@ def main():
         def step():
             fa.fa_fwd(qd, kd, vd, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
 
+    # Clock warm-up: untimed steps until S seconds have passed (checked every 16 launches,
+    # so the queue never runs dry), then the W counted warm-up steps.
+    clock_steps = 0
+    t_clock = time.perf_counter()
+    while time.perf_counter() - t_clock < args.warmup_seconds:
+        for _ in range(16):
+            step()
+        clock_steps += 16
+        torch.cuda.synchronize()
+    t_clock = time.perf_counter() - t_clock
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -426,6 +440,9 @@ def main():
             "algorithmic_bytes_per_launch": io_bytes,
         },
         "wall_s_timed": round(t_wall, 4),
+        "clock_warmup": {"seconds": round(t_clock, 3), "steps": clock_steps,
+                         "why": "untimed steps before the warm-up steps: the GPU clock ramps up "
+                                "under sustained load"},
         "cpu_baseline": None,
     }
     if bwd:
