@@ -32,7 +32,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 2,      /* head dimension not supported by the entry point, or a size too large */
   FA_ERR_MISALIGNED = 3,       /* a buffer not 16-byte aligned */
   FA_ERR_LAUNCH = 4,           /* the HIP runtime refused the kernel launch */
-  FA_ERR_JIT = 5               /* run-time compilation or loading of a specialized kernel failed */
+  FA_ERR_JIT = 5,              /* run-time compilation or loading of a specialized kernel failed */
+  FA_ERR_SCRATCH_LIMIT = 6     /* fa_bwd_noalloc: the problem needs more than its static workspace */
 } fa_status_t;
 
 /* Element type of Q, K, V and O. */
@@ -188,6 +189,26 @@ fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const void *O, c
                    const void *dO, void *dQ, void *dK, void *dV, float *work,
                    int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                    void *stream, int dtype);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, without the `work` argument. The
+ * 2*B*H*N-float workspace is a static array inside the library, one per GPU,
+ * held until the process ends: at most 2^21 floats (8 MiB), so
+ * B*H*N <= 2^20 rows (else FA_ERR_SCRATCH_LIMIT, nothing enqueued). The call
+ * allocates nothing, on the host or the device. Every call on one GPU uses that
+ * GPU's array; each call rewrites every entry it reads (per row: the sum over c
+ * of dO*O, then L * log2 e) before reading it, so nothing carries over between
+ * calls, but calls that overlap in time on one GPU (different streams, or
+ * several host threads) race on the array and must be serialized by the
+ * caller. FA_ERR_LAUNCH if the array's device address cannot be obtained.
+ * Every other argument, requirement and status as for fa_bwd.
+ */
+fa_status_t fa_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O, const float *L,
+                           const void *dO, void *dQ, void *dK, void *dV,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                           void *stream, int dtype);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -22,8 +22,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_specialized", "fa_fwd_strided", "fa_jit_code_object",
-                                    "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_specialized", "fa_fwd_strided",
+                                    "fa_jit_code_object", "fa_status_string", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert fa.fa_status_string(0) == "ok"
-    for s in range(1, 6):
+    for s in range(1, 7):
         assert fa.fa_status_string(s) not in ("ok", "unknown status")
     assert fa.fa_status_string(99) == "unknown status"
     assert fa.fa_version() >= 100
@@ -131,6 +131,32 @@ def test_bwd_overlapping_outputs(kw):
 @pytest.mark.parametrize("name", ["Q", "dO", "dK", "work", "L"])
 def test_bwd_misaligned(name):
     assert call_bwd(**{name: BWD[name] + 4}) == fa.FA_ERR_MISALIGNED
+
+
+# fa_bwd_noalloc: the same checks as fa_bwd (no workspace argument), and a size limit of
+# 2^20 rows (B*H*N) checked first, before the library's workspace is looked up.
+def call_bwd_noalloc(B=1, H=1, N=64, d=64, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16, **kw):
+    p = dict(BWD, **kw)
+    return fa.raw_fa_bwd_noalloc(p["Q"], p["K"], p["V"], p["O"], p["L"], p["dO"], p["dQ"], p["dK"], p["dV"],
+                                 B, H, N, d, causal, scale, None, dtype)
+
+
+@pytest.mark.parametrize("kw", [dict(N=(1 << 20) + 1), dict(B=2, H=4, N=(1 << 17) + 1), dict(B=1 << 21),
+                                dict(B=1 << 40, H=1 << 40), dict(N=1 << 24)])
+def test_bwd_noalloc_size_limit(kw):
+    assert call_bwd_noalloc(**kw) == fa.FA_ERR_SCRATCH_LIMIT
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(H=-1), dict(Q=0), dict(dV=0), dict(scale=0.0),
+                                dict(dtype=7), dict(dK=6 * A), dict(dQ=2 * A + 64)])
+def test_bwd_noalloc_bad_arguments(kw):
+    assert call_bwd_noalloc(**kw) == fa.FA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw,status", [(dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+                                       (dict(dO=6 * A + 4), fa.FA_ERR_MISALIGNED)])
+def test_bwd_noalloc_validation(kw, status):
+    assert call_bwd_noalloc(**kw) == status
 
 
 # fa_fwd_strided: every call below fails validation, so nothing is ever launched on

@@ -1,7 +1,7 @@
 """Tiled online-softmax attention forward and backward passes for MI355X (gfx950).
 
-``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_specialized`` and ``fa_bwd`` mirror the C
-entry points of ``libfa.so``; ``forward``, ``forward_strided``, ``forward_specialized``
+``fa_fwd``, ``fa_fwd_strided``, ``fa_fwd_specialized``, ``fa_bwd`` and ``fa_bwd_noalloc``
+mirror the C entry points of ``libfa.so``; ``forward``, ``forward_strided``, ``forward_specialized``
 and ``backward`` allocate the outputs (and the backward workspace) and call them;
 ``attention`` is the differentiable form (fa_fwd forward, fa_bwd backward).
 Importing fails loudly when the HIP library is not built.
@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     FA_ERR_JIT,
     FA_ERR_LAUNCH,
     FA_ERR_MISALIGNED,
+    FA_ERR_SCRATCH_LIMIT,
     FA_ERR_UNSUPPORTED,
     FA_OK,
     LIB_PATH,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     attention,
     backward,
     fa_bwd,
+    fa_bwd_noalloc,
     fa_fwd,
     fa_fwd_specialized,
     fa_fwd_strided,
@@ -31,6 +33,7 @@ from ._binding import (  # noqa: F401
     forward_strided,
     jit_code_object,
     raw_fa_bwd,
+    raw_fa_bwd_noalloc,
     raw_fa_fwd,
     raw_fa_fwd_specialized,
     raw_fa_fwd_strided,

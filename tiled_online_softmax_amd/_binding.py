@@ -22,6 +22,7 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_MISALIGNED = 3
 FA_ERR_LAUNCH = 4
 FA_ERR_JIT = 5
+FA_ERR_SCRATCH_LIMIT = 6
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 
@@ -46,6 +47,11 @@ _lib.fa_jit_code_object.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, 
                                     ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
 _lib.fa_bwd.restype = ctypes.c_int
 _lib.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
+    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+    ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+]
+_lib.fa_bwd_noalloc.restype = ctypes.c_int
+_lib.fa_bwd_noalloc.argtypes = [ctypes.c_void_p] * 9 + [
     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
     ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
 ]
@@ -115,6 +121,12 @@ def raw_fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, s
     """The C backward entry point with integer pointers; returns the status code."""
     return int(_lib.fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, int(causal),
                            float(scale), stream, int(dtype)))
+
+
+def raw_fa_bwd_noalloc(Q, K, V, O, L, dO, dQ, dK, dV, B, H, N, d, causal, scale, stream, dtype) -> int:
+    """The allocation-free C backward entry point with integer pointers; returns the status code."""
+    return int(_lib.fa_bwd_noalloc(Q, K, V, O, L, dO, dQ, dK, dV, B, H, N, d, int(causal),
+                                   float(scale), stream, int(dtype)))
 
 
 _DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
@@ -271,6 +283,26 @@ def fa_bwd(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, strea
                     _stream_handle(stream, Q.device), _DTYPES[dt])
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_noalloc(Q, K, V, O, L, dO, dQ, dK, dV, B, H, N, d, causal, scale, stream=None):
+    """fa_bwd without a workspace argument: the library's static per-GPU workspace is used
+    (B*H*N <= 2^20 rows; calls that overlap in time on one GPU race on it). Same tensor
+    requirements as fa_bwd. Raises FaError on a bad argument or a too-large problem."""
+    dt = Q.dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}")
+    for t in (Q, K, V, O, dO, dQ, dK, dV):
+        if t.dtype != dt or tuple(t.shape) != (B, H, N, d) or not t.is_contiguous():
+            raise ValueError("Q, K, V, O, dO, dQ, dK, dV must be contiguous [B, H, N, d] tensors of one dtype")
+        if t.device.type != "cuda" or t.device != Q.device:
+            raise ValueError("all tensors must live on the same GPU")
+    if L.dtype != torch.float32 or tuple(L.shape) != (B, H, N) or not L.is_contiguous() or L.device != Q.device:
+        raise ValueError("L must be a contiguous fp32 [B, H, N] tensor on the same GPU")
+    st = raw_fa_bwd_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(L), _ptr(dO), _ptr(dQ), _ptr(dK),
+                            _ptr(dV), B, H, N, d, causal, scale, _stream_handle(stream, Q.device), _DTYPES[dt])
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
 
 
 def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None):

@@ -41,6 +41,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa.h"
@@ -829,13 +830,13 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-}  // namespace
 
-extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const void *O,
-                              const float *L, const void *dO, void *dQ, void *dK, void *dV,
-                              float *work, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
-                              float scale, void *stream, int dtype) {
-  if (!Q || !K || !V || !O || !L || !dO || !dQ || !dK || !dV || !work)
+// Checks fa_bwd's arguments. `work` (2 * B * H * N floats of caller workspace)
+// is checked only when `has_work`; the library's own workspace overlaps nothing.
+fa_status_t bwd_validate(const void *Q, const void *K, const void *V, const void *O, const float *L,
+                         const void *dO, void *dQ, void *dK, void *dV, const float *work, bool has_work,
+                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, int dtype) {
+  if (!Q || !K || !V || !O || !L || !dO || !dQ || !dK || !dV || (has_work && !work))
     return FA_ERR_INVALID_ARGUMENT;
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARGUMENT;
   if (!(scale > 0.f) || !isfinite((float)((double)scale * 1.4426950408889634074)))  // finite scale * log2(e)
@@ -857,19 +858,28 @@ extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const
   for (void *o : outs) {
     for (const void *i : ins)
       if (overlaps(o, tbytes, i, tbytes)) return FA_ERR_INVALID_ARGUMENT;
-    if (overlaps(o, tbytes, L, lbytes) || overlaps(o, tbytes, work, 2 * lbytes))
+    if (overlaps(o, tbytes, L, lbytes) || (has_work && overlaps(o, tbytes, work, 2 * lbytes)))
       return FA_ERR_INVALID_ARGUMENT;
   }
   if (overlaps(dQ, tbytes, dK, tbytes) || overlaps(dQ, tbytes, dV, tbytes) ||
       overlaps(dK, tbytes, dV, tbytes))
     return FA_ERR_INVALID_ARGUMENT;
-  for (const void *i : ins)
-    if (overlaps(work, 2 * lbytes, i, tbytes)) return FA_ERR_INVALID_ARGUMENT;
-  if (overlaps(work, 2 * lbytes, L, lbytes)) return FA_ERR_INVALID_ARGUMENT;
+  if (has_work) {
+    for (const void *i : ins)
+      if (overlaps(work, 2 * lbytes, i, tbytes)) return FA_ERR_INVALID_ARGUMENT;
+    if (overlaps(work, 2 * lbytes, L, lbytes)) return FA_ERR_INVALID_ARGUMENT;
+  }
   if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)L | (uintptr_t)dO |
-       (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV | (uintptr_t)work) & 15)
+       (uintptr_t)dQ | (uintptr_t)dK | (uintptr_t)dV | (has_work ? (uintptr_t)work : 0)) & 15)
     return FA_ERR_MISALIGNED;
+  return FA_OK;
+}
 
+// Enqueues the three kernels for validated arguments.
+fa_status_t bwd_launch(const void *Q, const void *K, const void *V, const void *O, const float *L,
+                       const void *dO, void *dQ, void *dK, void *dV, float *work, int64_t B, int64_t H,
+                       int64_t N, int64_t d, int causal, float scale, void *stream, int dtype) {
+  const bool bf = dtype == FA_DTYPE_BF16;
   const float c = (float)((double)scale * 1.4426950408889634074);  // scale * log2(e)
   hipStream_t s = (hipStream_t)stream;
   const int n = (int)N;
@@ -894,4 +904,59 @@ extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const
                    : launch_bwd_f32<128, false>(BH, n, s, Q, K, V, O, L, dO, dQ, dK, dV, work, c, scale);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+// Workspace of the allocation-free entry point: one array per GPU, for the
+// process's lifetime, shared by every fa_bwd_noalloc call on that GPU. In host
+// code `scratch` names a host-side stand-in; the device address is fetched with
+// hipGetSymbolAddress and used everywhere instead.
+constexpr int64_t kBwdScratchFloats = (int64_t)1 << 21;  // 8 MiB: B * H * N <= 2^20 rows
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once fetched
+
+// The device address of the current device's copy of `scratch` (fetched on the
+// first call on that device, with it current), or null on failure.
+float *device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = (float *)ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const void *O,
+                              const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                              float *work, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                              float scale, void *stream, int dtype) {
+  const fa_status_t st = bwd_validate(Q, K, V, O, L, dO, dQ, dK, dV, work, true, B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  return bwd_launch(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, stream, dtype);
+}
+
+extern "C" fa_status_t fa_bwd_noalloc(const void *Q, const void *K, const void *V, const void *O,
+                                      const float *L, const void *dO, void *dQ, void *dK, void *dV,
+                                      int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                      float scale, void *stream, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARGUMENT;
+  if (B > kBwdScratchFloats || H > kBwdScratchFloats || N > kBwdScratchFloats ||
+      2 * B * H * N > kBwdScratchFloats)
+    return FA_ERR_SCRATCH_LIMIT;
+  const fa_status_t st = bwd_validate(Q, K, V, O, L, dO, dQ, dK, dV, nullptr, false, B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  float *work = device_scratch();
+  if (!work) return FA_ERR_LAUNCH;
+  return bwd_launch(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, stream, dtype);
 }

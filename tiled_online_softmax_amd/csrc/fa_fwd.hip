@@ -446,6 +446,7 @@ extern "C" const char *fa_status_string(int status) {
     case FA_ERR_MISALIGNED: return "buffer not 16-byte aligned";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_JIT: return "run-time compilation of a specialized kernel failed";
+    case FA_ERR_SCRATCH_LIMIT: return "problem larger than the static workspace of fa_bwd_noalloc";
     default: return "unknown status";
   }
 }
