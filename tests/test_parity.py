@@ -209,6 +209,25 @@ def test_grid_not_multiple_of_xcds(fa, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_head_groups_per_xcd(fa, causal):
+    """48 heads of N=4096, d=128 (2 MiB of K and V each): six heads per XCD, which each XCD
+    takes three at a time (the largest divisor of 6 whose K and V fit in 8 MiB), so every
+    XCD runs two head groups. O and L start as NaN, so a tile the mapping skips shows as a
+    non-finite row; every row of every head is compared with the oracle."""
+    B, H, N, d = 3, 16, 4096, 128
+    q, k, v = make_qkv(B, H, N, d, "bf16", seed=48)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    O = torch.full_like(qd, float("nan"))
+    L = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+    fa.fa_fwd(qd, kd, vd, O, L, B, H, N, d, causal, default_scale(d))
+    torch.cuda.synchronize()
+    label = f"B{B} H{H} N{N} d{d} causal={causal}"
+    eo, el = _errors_by_head(O, L, q, k, v, causal, default_scale(d), label)
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1], f"{label}: O error {eo}, L error {el}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_scale_other_than_default(fa, causal):
     q, k, v = make_qkv(1, 2, 300, 128, "bf16", seed=43)
     _check(fa, q, k, v, causal, 0.3, "bf16", label=f"scale 0.3 causal={causal}")

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
   const int l32 = lane % 32, hh = lane / 32;
 
   int bh, qt;
-  map_block(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, bh, qt);
+  map_block(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, 0, bh, qt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const bf16 *Kh = K + head;
   const bf16 *Vh = V + head;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_bf16_kernel(
 
   // Key tiles in ascending order: when causal, the first ones see the most queries.
   int bh, kt;
-  map_block(blockIdx.x, gridDim.x, n_ktiles, false, bh, kt);
+  map_block(blockIdx.x, gridDim.x, n_ktiles, false, 0, bh, kt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const bf16 *Qh = Q + head;
   const bf16 *Gh = dO + head;
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_f32_kernel(
   const int lane = tid % 64, l32 = lane % 32, hh = lane / 32;
 
   int bh, qb;
-  map_block(blockIdx.x, gridDim.x, n_qblocks, CAUSAL, bh, qb);
+  map_block(blockIdx.x, gridDim.x, n_qblocks, CAUSAL, 0, bh, qb);
   const size_t head = (size_t)bh * (size_t)N * D;
   const float *Kh = K + head;
   const float *Vh = V + head;
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_f32_kernel(
 
   // Key blocks in ascending order: when causal, the first ones see the most queries.
   int bh, kb;
-  map_block(blockIdx.x, gridDim.x, n_kblocks, false, bh, kb);
+  map_block(blockIdx.x, gridDim.x, n_kblocks, false, 0, bh, kb);
   const size_t head = (size_t)bh * (size_t)N * D;
   const float *Qh = Q + head;
   const float *Gh = dO + head;

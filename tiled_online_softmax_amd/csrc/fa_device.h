@@ -51,20 +51,25 @@ __device__ __forceinline__ float halves_sum(float x) {
 // Workgroup index -> (head, query tile). Workgroups are dispatched to the
 // eight XCDs round-robin (XCD = bid % 8, in order bid / 8 within an XCD).
 // When the heads split evenly over the XCDs, XCD x takes heads
-// [x*hpx, (x+1)*hpx), so each head's K/V stays in one XCD's L2; within an XCD,
-// and globally otherwise, work is ordered by query tile, all heads at one
-// tile before the next. For causal attention the tiles run from the last
+// [x*hpx, (x+1)*hpx), so each head's K/V stays in one XCD's L2, and works on
+// them `group` heads at a time (group divides hpx; 0 or any other value: all
+// hpx at once): the heads of one group, ordered by query tile, all heads at
+// one tile before the next, then the next group. Otherwise the whole grid is
+// ordered by query tile. For causal attention the tiles run from the last
 // query tile (most key tiles) to the first, so the longest workgroups start
 // first and the short ones fill the tail.
-__device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bool causal,
+__device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bool causal, int group,
                                           int &bh, int &qt) {
   const int n_heads = nblocks / n_qtiles;
   int t;
   if (n_heads % kNumXcd == 0) {
     const int hpx = n_heads / kNumXcd;
+    const int g = (group > 0 && hpx % group == 0) ? group : hpx;
     const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
-    t = slot / hpx;
-    bh = xcd * hpx + slot % hpx;
+    const int per = g * n_qtiles;  // workgroups of one group
+    const int grp = slot / per, r = slot - grp * per;
+    t = r / g;
+    bh = xcd * hpx + grp * g + r % g;
   } else {
     t = bid / n_heads;
     bh = bid % n_heads;

@@ -17,6 +17,7 @@
 
 #include <hip/hiprtc.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -29,6 +30,21 @@
 #include "fa_jit_source.inc"
 
 namespace {
+
+// Heads that each XCD works on at a time (map_block): the largest divisor of
+// the XCD's heads whose K and V, kv_bytes per head, total at most 8 MiB (at
+// least one head); 0 (no grouping) when the heads do not split evenly over the
+// XCDs. An XCD's L2 is 4 MB: with all of the XCD's heads at once the causal
+// workloads read K and V from HBM 4-7 times over; with groups of 8 MiB their
+// concurrent workgroups share each group's tiles closely enough in time.
+constexpr int64_t kHeadGroupBytes = (int64_t)8 << 20;
+int head_group(int64_t BH, int64_t kv_bytes) {
+  if (BH % kNumXcd != 0) return 0;
+  const int64_t hpx = BH / kNumXcd;
+  int64_t g = std::min<int64_t>({hpx, 4096, std::max<int64_t>(1, kHeadGroupBytes / std::max<int64_t>(1, kv_bytes))});
+  while (hpx % g != 0) --g;
+  return (int)g;
+}
 
 hipError_t launch(const void *kern, int64_t nblocks, int threads, hipStream_t stream, FwdParams p) {
   void *args[] = {(void *)&p};
@@ -69,6 +85,7 @@ int64_t bf16_rows(int64_t BH, int64_t Nq, bool causal) {
 
 template <int D, bool CAUSAL>
 hipError_t launch_bf16(int64_t BH, hipStream_t s, FwdParams p) {
+  p.head_group = head_group(BH, (int64_t)p.Nk * D * 2 * 2);
   if (bf16_small_grid(BH, p.Nq, CAUSAL)) {
     constexpr int rows = kBf16Rows / kBf16SmallGridSplit;
     p.n_qtiles = (p.Nq + rows - 1) / rows;
@@ -88,6 +105,7 @@ constexpr int kF32Waves = FA_F32_NW;
 
 template <int D, bool CAUSAL>
 hipError_t launch_f32(int64_t BH, hipStream_t s, FwdParams p) {
+  p.head_group = head_group(BH, (int64_t)p.Nk * D * 4 * 2);
   p.n_qtiles = (p.Nq + kF32Rows - 1) / kF32Rows;
   const void *kern = (const void *)&fa_fwd_f32_kernel<D, CAUSAL, kF32Waves>;
   return launch(kern, BH * p.n_qtiles, 64 * kF32Waves, s, p);
@@ -332,6 +350,7 @@ extern "C" fa_status_t fa_fwd_specialized(const void *Q, const void *K, const vo
   FwdParams p = contiguous_params(Q, K, V, O, L, H, N, d, scale);
   const int64_t rows = block_rows(dtype, B * H, N, causal != 0);
   p.n_qtiles = (int)((N + rows - 1) / rows);
+  p.head_group = head_group(B * H, N * d * (dtype == FA_DTYPE_BF16 ? 2 : 4) * 2);
   void *args[] = {(void *)&p};
   const hipError_t err = hipModuleLaunchKernel(kern.function, (unsigned)(B * H * p.n_qtiles), 1, 1,
                                                (unsigned)block_threads(dtype), 1, 1, 0, (hipStream_t)stream,

@@ -40,7 +40,9 @@
 //    blocks wholly after a wave's rows are skipped by that wave, and the mask
 //    is evaluated only on blocks that straddle the diagonal or the ragged end.
 //  * The workgroup index is remapped so that the eight XCDs each own whole
-//    heads (their L2 keeps that head's K/V), heaviest causal tiles first.
+//    heads (their L2 keeps that head's K/V) and take them a few at a time
+//    (the heads whose K and V total at most 8 MiB), heaviest causal tiles
+//    first.
 //
 // Shape specialization: when FA_SPEC_NQ is defined (hipRTC builds), the row
 // counts, the batch and head counts and the strides of a contiguous
@@ -95,7 +97,8 @@ struct FwdParams {
   int64_t q_b, q_h, k_b, k_h, v_b, v_h, o_b, o_h, l_b, l_h;
   int q_r, k_r, v_r, o_r, l_r;
   int H, Nq, Nk, n_qtiles;
-  float c;  // scale * log2(e)
+  int head_group;  // heads an XCD works on at a time (map_block)
+  float c;         // scale * log2(e)
 };
 
 // The sizes and strides a kernel works with: the parameter block's fields, or,
@@ -109,21 +112,22 @@ struct Shape {
   static constexpr int q_r = D, k_r = D, v_r = D, o_r = D, l_r = 1;
   static constexpr int64_t q_h = (int64_t)Nq * D, k_h = (int64_t)Nk * D, v_h = k_h, o_h = q_h, l_h = Nq;
   static constexpr int64_t q_b = H * q_h, k_b = H * k_h, v_b = k_b, o_b = q_b, l_b = H * l_h;
-  __device__ explicit Shape(const FwdParams &) {}
+  int group;
+  __device__ explicit Shape(const FwdParams &p) : group(p.head_group) {}
   // Workgroup -> (batch * head, query tile); the grid size is a constant too.
   __device__ void place(bool causal, int &bh, int &qt) const {
-    map_block(blockIdx.x, B * H * n_qtiles, n_qtiles, causal, bh, qt);
+    map_block(blockIdx.x, B * H * n_qtiles, n_qtiles, causal, group, bh, qt);
   }
 #else
-  int H, Nq, Nk, n_qtiles;
+  int H, Nq, Nk, n_qtiles, group;
   int q_r, k_r, v_r, o_r, l_r;
   int64_t q_h, k_h, v_h, o_h, l_h, q_b, k_b, v_b, o_b, l_b;
   __device__ explicit Shape(const FwdParams &p)
-      : H(p.H), Nq(p.Nq), Nk(p.Nk), n_qtiles(p.n_qtiles), q_r(p.q_r), k_r(p.k_r), v_r(p.v_r), o_r(p.o_r),
-        l_r(p.l_r), q_h(p.q_h), k_h(p.k_h), v_h(p.v_h), o_h(p.o_h), l_h(p.l_h), q_b(p.q_b), k_b(p.k_b),
+      : H(p.H), Nq(p.Nq), Nk(p.Nk), n_qtiles(p.n_qtiles), group(p.head_group), q_r(p.q_r), k_r(p.k_r),
+        v_r(p.v_r), o_r(p.o_r), l_r(p.l_r), q_h(p.q_h), k_h(p.k_h), v_h(p.v_h), o_h(p.o_h), l_h(p.l_h), q_b(p.q_b), k_b(p.k_b),
         v_b(p.v_b), o_b(p.o_b), l_b(p.l_b) {}
   __device__ void place(bool causal, int &bh, int &qt) const {
-    map_block(blockIdx.x, gridDim.x, n_qtiles, causal, bh, qt);
+    map_block(blockIdx.x, gridDim.x, n_qtiles, causal, group, bh, qt);
   }
 #endif
 };
