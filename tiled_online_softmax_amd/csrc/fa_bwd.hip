@@ -149,7 +149,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ work, bf16 *__restrict__ dQ, int N,
-    int n_qtiles, int64_t rows, float c, float scale) {
+    int n_qtiles, int64_t rows, float c, float scale, int group) {
   using LY = BfLayout<D, kBwdTile, 4>;
   constexpr int BN = kBwdTile;
   constexpr int NKB = BN / 32;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
   const int l32 = lane % 32, hh = lane / 32;
 
   int bh, qt;
-  map_block(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, 0, bh, qt);
+  map_block(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, group, bh, qt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const bf16 *Kh = K + head;
   const bf16 *Vh = V + head;
@@ -276,7 +276,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_bf16_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const float *__restrict__ work, bf16 *__restrict__ dK,
-    bf16 *__restrict__ dV, int N, int n_ktiles, int64_t rows, float c, float scale) {
+    bf16 *__restrict__ dV, int N, int n_ktiles, int64_t rows, float c, float scale, int group) {
   constexpr int NW = 8;
   using LY = BfLayout<D, kBwdTile, NW>;   // streamed Q, dO tiles
   using LK = BfLayout<D, kBwdRows, NW>;   // the workgroup's K, V rows
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_bf16_kernel(
 
   // Key tiles in ascending order: when causal, the first ones see the most queries.
   int bh, kt;
-  map_block(blockIdx.x, gridDim.x, n_ktiles, false, 0, bh, kt);
+  map_block(blockIdx.x, gridDim.x, n_ktiles, false, group, bh, kt);
   const size_t head = (size_t)bh * (size_t)N * D;
   const bf16 *Qh = Q + head;
   const bf16 *Gh = dO + head;
@@ -787,6 +787,8 @@ hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, cons
                            void *dK, void *dV, float *work, float c, float scale) {
   const int64_t rows = BH * N;
   const int ntiles = (N + kBwdRows - 1) / kBwdRows;
+  // Both kernels stream two bf16 N x D matrices per head (K, V or Q, dO).
+  const int group = head_group(BH, (int64_t)N * D * 2 * 2);
   constexpr int prep_rows = 256 / (D / 8);
   hipLaunchKernelGGL((fa_bwd_prep_kernel<bf16, D>), dim3((unsigned)((rows + prep_rows - 1) / prep_rows)), dim3(256), 0, s,
                      (const bf16 *)O, (const bf16 *)dO, L, work, rows);
@@ -794,12 +796,12 @@ hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, cons
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(256), 0, s,
                      (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
-                     (bf16 *)dQ, N, ntiles, rows, c, scale);
+                     (bf16 *)dQ, N, ntiles, rows, c, scale, group);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(512), 0, s,
                      (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
-                     (bf16 *)dK, (bf16 *)dV, N, ntiles, rows, c, scale);
+                     (bf16 *)dK, (bf16 *)dV, N, ntiles, rows, c, scale, group);
   return hipGetLastError();
 }
 

@@ -77,6 +77,27 @@ __device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bo
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
+#if !defined(__HIPCC_RTC__)
+// Host side of map_block: the heads each XCD works on at a time, the largest
+// divisor of the XCD's heads whose streamed tiles (tile_bytes per head: K and V
+// in the forward and the dQ kernel, Q and dO in the dK/dV kernel) total at most
+// 8 MiB, at least one head; 0 (no grouping) when the heads do not split evenly
+// over the XCDs. An XCD's L2 is 4 MB: with all of an XCD's heads at once the
+// causal workloads read their tiles from HBM 4-7 times over; with groups of
+// 8 MiB the concurrent workgroups of a group share its tiles closely enough in
+// time (groups of 4 MiB fetch less but run slower).
+inline int head_group(int64_t BH, int64_t tile_bytes) {
+  constexpr int64_t kGroupBytes = (int64_t)8 << 20;
+  if (BH % kNumXcd != 0) return 0;
+  const int64_t hpx = BH / kNumXcd;
+  const int64_t fit = kGroupBytes / (tile_bytes > 0 ? tile_bytes : 1);
+  int64_t g = hpx < 4096 ? hpx : 4096;
+  if (g > fit) g = fit > 0 ? fit : 1;
+  while (hpx % g != 0) --g;
+  return (int)g;
+}
+#endif
+
 // Layout of a bf16 tile of BN rows x D columns staged in LDS (rows of K, V, Q
 // or dO). Rows are written by LDS DMA in 1 KiB wave instructions; inside a row
 // the 16-byte chunks are XOR-permuted by one of two row functions, chosen per

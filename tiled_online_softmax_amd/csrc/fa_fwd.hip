@@ -31,21 +31,6 @@
 
 namespace {
 
-// Heads that each XCD works on at a time (map_block): the largest divisor of
-// the XCD's heads whose K and V, kv_bytes per head, total at most 8 MiB (at
-// least one head); 0 (no grouping) when the heads do not split evenly over the
-// XCDs. An XCD's L2 is 4 MB: with all of the XCD's heads at once the causal
-// workloads read K and V from HBM 4-7 times over; with groups of 8 MiB their
-// concurrent workgroups share each group's tiles closely enough in time.
-constexpr int64_t kHeadGroupBytes = (int64_t)8 << 20;
-int head_group(int64_t BH, int64_t kv_bytes) {
-  if (BH % kNumXcd != 0) return 0;
-  const int64_t hpx = BH / kNumXcd;
-  int64_t g = std::min<int64_t>({hpx, 4096, std::max<int64_t>(1, kHeadGroupBytes / std::max<int64_t>(1, kv_bytes))});
-  while (hpx % g != 0) --g;
-  return (int)g;
-}
-
 hipError_t launch(const void *kern, int64_t nblocks, int threads, hipStream_t stream, FwdParams p) {
   void *args[] = {(void *)&p};
   return hipLaunchKernel(kern, dim3((unsigned)nblocks), dim3(threads), args, 0, stream);
