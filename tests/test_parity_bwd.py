@@ -125,6 +125,37 @@ def test_bwd_heads(fa, B, H, N, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_bwd_head_groups_per_xcd(fa, causal):
+    """96 heads of N=2048, d=128 (1 MiB per streamed matrix): twelve heads per XCD, which
+    both kernels take six at a time (the largest divisor of 12 whose streamed tiles fit in
+    8 MiB), so every XCD runs two head groups. dQ, dK and dV start as NaN, so a tile the
+    mapping skips shows as a non-finite row; heads from each group position of XCDs 0, 1
+    and 7 are compared with the oracle (a head's gradients depend on that head alone)."""
+    B, H, N, d = 2, 48, 2048, 128
+    q, k, v, do = _inputs(B, H, N, d, seed=2150 + causal)
+    scale = default_scale(d)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    O, L = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = (torch.full_like(qd, float("nan")) for _ in range(3))
+    work = torch.empty(2 * B * H * N, dtype=torch.float32, device=dev)
+    fa.fa_bwd(qd, kd, vd, O, L, dod, dq, dk, dv, work, B, H, N, d, causal, scale)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t).all(), f"{name} has rows no workgroup wrote"
+    tol = TOL["bf16"]
+    for bh in (0, 5, 6, 11, 12, 23, 84, 95):
+        b, h = divmod(bh, H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref, stored = stored_statistics_gradient(q[sl], k[sl], v[sl], do[sl], O[sl], L[sl], causal, scale)
+        for name, a, r, s in zip(("dQ", "dK", "dV"), (dq[sl], dk[sl], dv[sl]), ref, stored):
+            err = float(np.abs(a.double().cpu().numpy() - s).max())
+            bound = tol * max(1.0, float(np.abs(r).max()))
+            print(f"[parity-bwd] head {bh} causal={causal} {name} max|err|={err:.3e} (tol {bound:.3e})", flush=True)
+            assert err <= bound, f"head {bh}: {name} error {err} > {bound}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_bwd_long_sequence(fa, causal):
     """N = 4096 at d = 128: 32 key tiles per dQ workgroup, 64 query tiles per dK/dV workgroup."""
     q, k, v, do = _inputs(1, 2, 4096, 128, seed=2200 + causal)
