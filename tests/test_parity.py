@@ -227,6 +227,35 @@ def test_head_groups_per_xcd(fa, causal):
     assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1], f"{label}: O error {eo}, L error {el}"
 
 
+@pytest.mark.parametrize("B,H,N,d,causal,group", [
+    (2, 32, 2304, 128, True, 4),    # 8 heads per XCD, 1.2 MB of K/V each: two groups of 4
+    (1, 40, 4096, 64, False, 5),    # 5 heads per XCD, 1 MiB each: one group of all 5
+    (1, 40, 8192, 128, True, 1),    # 4 MiB each: one head at a time, 5 groups
+    (3, 8, 3000, 128, False, 3),    # 3 heads per XCD, 1.5 MB each: one group of 3
+    (1, 72, 2048, 128, True, 3),    # 9 heads per XCD, 1 MiB each: 8 would fit, 3 divides 9
+])
+def test_head_group_sizes(fa, B, H, N, d, causal, group):
+    """The per-XCD head groups over a range of group sizes (the largest divisor of the XCD's
+    head count whose K and V fit in 8 MiB; the comment gives it). O and L start as NaN, so a
+    tile the mapping skips shows as a non-finite row; 24 rows of every head against the
+    oracle."""
+    q, k, v = make_qkv(B, H, N, d, "bf16", seed=49 + H + N)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    O = torch.full_like(qd, float("nan"))
+    L = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev)
+    fa.fa_fwd(qd, kd, vd, O, L, B, H, N, d, causal, default_scale(d))
+    torch.cuda.synchronize()
+    assert torch.isfinite(O).all() and torch.isfinite(L).all(), "rows no workgroup wrote"
+    rows = np.unique(np.concatenate([np.linspace(0, N - 1, 20).astype(int), [1, 127, 128, N - 2]]))
+    Oref, Lref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                  causal, default_scale(d), rows=rows)
+    eo, el = _errors(O, L, Oref, Lref, rows)
+    label = f"B{B} H{H} N{N} d{d} causal={causal} (groups of {group})"
+    print(f"[parity] {label} max|dO|={eo:.3e} max|dL|={el:.3e}", flush=True)
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1], f"{label}: O error {eo}, L error {el}"
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_scale_other_than_default(fa, causal):
     q, k, v = make_qkv(1, 2, 300, 128, "bf16", seed=43)
