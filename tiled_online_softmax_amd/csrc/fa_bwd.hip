@@ -66,7 +66,9 @@ __device__ __forceinline__ void load_lds_4(__amdgpu_buffer_rsrc_t rsrc, uint32_t
 #endif
 }
 
-// Per-lane addressing of a 64-row bf16 tile laid out with swz_k (BfLayout).
+// Per-lane addressing of a bf16 tile laid out with swz_b (BfLayout): every tile
+// of the backward is read as rows, and the streamed K, Q and dO tiles also
+// transposed.
 //  * row reads: lane (l32, hh) reads chunk 2cc + hh of row 32 blk + l32 at
 //    tile + 32 blk ROW + (row_base ^ 32 cc);
 //  * transposing reads (ds_read_b64_tr_b16): the 16-lane group g reads rows
@@ -77,17 +79,18 @@ __device__ __forceinline__ void load_lds_4(__amdgpu_buffer_rsrc_t rsrc, uint32_t
 //    order in which the MFMA result layout lists a lane's 16 rows.
 template <class LY>
 struct TileAddr {
+  static_assert(LY::CPR == 8 || LY::CPR == 16, "swz_b is defined for d = 64 and 128");
   int row_base;
   int tr_base[2];
   __device__ TileAddr(int lane) {
     const int l32 = lane % 32, hh = lane / 32;
-    row_base = l32 * LY::ROW + 16 * (hh ^ LY::swz_k(l32));
+    row_base = l32 * LY::ROW + 16 * (hh ^ LY::swz_b(l32));
     const int trow = 4 * hh + (lane % 16) / 4;
     const int tcol = 32 * ((lane / 16) % 2) + 8 * (lane % 4);
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
       const int r = 8 * hi + trow;
-      tr_base[hi] = r * LY::ROW + 16 * ((tcol >> 4) ^ LY::swz_k(r)) + (tcol & 15);
+      tr_base[hi] = r * LY::ROW + 16 * ((tcol >> 4) ^ LY::swz_b(r)) + (tcol & 15);
     }
   }
   __device__ bf16x8 row(const char *tile, int blk, int cc) const {
@@ -102,7 +105,7 @@ struct TileAddr {
 };
 
 // Per-lane global byte offsets of this wave's share of a 64-row tile load (LDS
-// slot p = 1024 gi + 16 lane holds chunk slot ^ swz_k(row) of row p / ROW);
+// slot p = 1024 gi + 16 lane holds chunk slot ^ swz_b(row) of row p / ROW);
 // load i adds 1024 i through its instruction offset, so it is taken out here.
 template <class LY>
 __device__ __forceinline__ void tile_load_offsets(int wave, int lane, int (&vo)[LY::LPW]) {
@@ -110,7 +113,7 @@ __device__ __forceinline__ void tile_load_offsets(int wave, int lane, int (&vo)[
   for (int i = 0; i < LY::LPW; ++i) {
     const int p = 64 * (wave * LY::LPW + i) + lane;
     const int r = p / LY::CPR, j = p % LY::CPR;
-    vo[i] = r * LY::ROW + 16 * (j ^ LY::swz_k(r)) - 1024 * i;
+    vo[i] = r * LY::ROW + 16 * (j ^ LY::swz_b(r)) - 1024 * i;
   }
 }
 

@@ -100,13 +100,19 @@ inline int head_group(int64_t BH, int64_t tile_bytes) {
 
 // Layout of a bf16 tile of BN rows x D columns staged in LDS (rows of K, V, Q
 // or dO). Rows are written by LDS DMA in 1 KiB wave instructions; inside a row
-// the 16-byte chunks are XOR-permuted by one of two row functions, chosen per
+// the 16-byte chunks are XOR-permuted by one of three row functions, chosen per
 // tile by how it is read:
 //  * swz_k, for ds_read_b128 of 32 consecutive rows at one chunk: spreads 16
 //    consecutive rows over the 16 slots of a 256-byte bank line;
 //  * swz_v, for ds_read_b64_tr_b16 (a 16-lane group reads 4 consecutive rows x
 //    32 bytes and its partner group the next 32 bytes): 4 * (row index within
-//    the group of 4), so the 4 x 4 chunks of a group pair land in 16 slots.
+//    the group of 4), so the 4 x 4 chunks of a group pair land in 16 slots;
+//  * swz_b, for tiles read both ways (d = 64 and 128 only): the row's position
+//    within its group of 4 sets chunk bits 2-3 (d = 128; at d = 64, where two
+//    rows share a bank line, its bit 1 sets chunk bit 2) and the group's index
+//    modulo 4 sets chunk bits 0-1, so both patterns fill each 256-byte bank
+//    line once per pass (swz_k leaves the transposing reads 4-way conflicted
+//    at d = 128 and 2-way at d = 64).
 template <int D, int BN, int NW>
 struct BfLayout {
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -120,6 +126,9 @@ struct BfLayout {
   static_assert(BN % 32 == 0, "key tile is a multiple of the 32-key MFMA block");
   __device__ static constexpr int swz_k(int r) { return (r / RPB) & (CPR - 1); }
   __device__ static constexpr int swz_v(int r) { return 4 * ((r / RPB) & (4 / RPB - 1)); }
+  __device__ static constexpr int swz_b(int r) {
+    return CPR == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
