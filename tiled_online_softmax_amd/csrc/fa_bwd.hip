@@ -363,13 +363,16 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_bf16_kernel(
     if (CAUSAL && EDGE && kw > qa + 31) return;  // every key of the wave after every query
 
     f32x16 s, dp;
-    // Each step's four operand reads stay next to its two MFMAs (the fence
-    // keeps the compiler from hoisting every read of the block into registers).
+    // At d = 64 each step's four operand reads stay next to its two MFMAs (the
+    // fence keeps the compiler from hoisting every read of the block into
+    // registers); at d = 128 the compiler's own order is faster (measured:
+    // 1.5% on the whole backward at d = 128, 5% slower without the fence at
+    // d = 64). The dV/dK products below are left to the compiler at both.
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(qs, qb, cc), ta.row(ks, kb, cc), cc == 0 ? f32x16{} : s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(gs, qb, cc), ta.row(vs, kb, cc), cc == 0 ? f32x16{} : dp, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (D == 64) __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -395,7 +398,6 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_dkdv_bf16_kernel(
       for (int db = 0; db < NDB; ++db) {
         dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(gs, qb, mm, db), pb[mm], dv[db], 0, 0, 0);
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.tr(qs, qb, mm, db), dsb[mm], dk[db], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
   };
 
