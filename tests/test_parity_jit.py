@@ -54,11 +54,15 @@ def test_specialized_matches_oracle_and_fa_fwd(fa, B, H, N, d, causal, dtype):
 
 
 def test_specialized_full_size_sampled(fa):
-    """The benchmarked causal bf16 B4 H16 N4096 d128 shape, sampled rows against the oracle."""
+    """The benchmarked causal bf16 B4 H16 N4096 d128 shape (each XCD takes its eight heads four at a
+    time): bitwise equal to fa_fwd on every element, sampled rows against the oracle."""
     w = WORKLOADS["causal_bf16_b4h16n4096d128"]
     q, k, v = w.make()
-    O, L = fa.forward_specialized(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=w.scale)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    O, L = fa.forward_specialized(qd, kd, vd, causal=True, scale=w.scale)
+    O2, L2 = fa.forward(qd, kd, vd, causal=True, scale=w.scale)
     torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(L, L2), "specialized and generic kernels differ"
     rows = sample_rows(w.N, 12, seed=w.seed)
     Oref, Lref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), True, w.scale,
                                   rows=rows)
