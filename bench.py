@@ -13,8 +13,8 @@ baseline times the fp64 oracle on a bounded sample of query rows on the host cor
 of the machine that runs the benchmark, and checks the sampled rows of the GPU output
 against it.
 
-``--pass bwd`` times the backward pass instead (one fa_bwd call: the preprocessing,
-dQ and dK/dV kernels) on the same workload with a seeded dO, with algorithmic
+``--pass bwd`` times the backward pass instead (one fa_bwd call: the dQ and dK/dV
+kernels, plus a preprocessing kernel for fp32) on the same workload with a seeded dO, with algorithmic
 FLOP = 8 d per admissible pair (the products dV = P^T dO, dP = dO V^T, dQ = dS K and
 dK = dS^T Q), and times the fp64 backward oracle on one head for the CPU baseline.
 """
@@ -446,7 +446,8 @@ def main():
         "cpu_baseline": None,
     }
     if bwd:
-        rec["roofline"]["kernel_ms"]["covers"] = "one fa_bwd call: preprocessing, dQ and dK/dV kernels"
+        rec["roofline"]["kernel_ms"]["covers"] = ("one fa_bwd call: dQ and dK/dV kernels" +
+                                                  (" and the preprocessing kernel" if w.dtype == "f32" else ""))
     if args.specialize:
         rec["config"]["specialized"] = True
         rec["jit_first_call_s"] = round(t_jit, 3)

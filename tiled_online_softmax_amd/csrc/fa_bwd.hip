@@ -14,8 +14,10 @@
 //    metal-flash-attention" page describes for that project's backward pass).
 //  * dS = P o (dP - D) with dP = dO V^T and D_i = sum_c dO[i][c] O[i][c]: the
 //    Jacobian of a row softmax applied to dP, using sum_j P[i][j] dP[i][j] =
-//    dO_i . sum_j P[i][j] V_j = dO_i . O_i. A preprocessing kernel forms D and
-//    the base-2 logsumexp L * log2 e once per row.
+//    dO_i . sum_j P[i][j] V_j = dO_i . O_i. D and the base-2 logsumexp
+//    L * log2 e are formed once per row: by the bf16 dQ kernel, which holds the
+//    row's dO already (it also stores them for the dK/dV kernel that runs
+//    after it), and by a preprocessing kernel for fp32.
 //
 // gfx950 mapping (bf16; v_mfma_f32_32x32x16_bf16, fp32 accumulation; P and dS
 // rounded to bf16 only as MFMA operands):
@@ -151,8 +153,9 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const T *__restrict__ 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
     const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const float *__restrict__ work, bf16 *__restrict__ dQ, int N,
-    int n_qtiles, int64_t rows, float c, float scale, int group) {
+    const bf16 *__restrict__ dO, const bf16 *__restrict__ O, const float *__restrict__ L,
+    float *__restrict__ work, bf16 *__restrict__ dQ, int N, int n_qtiles, int64_t rows, float c,
+    float scale, int group) {
   using LY = BfLayout<D, kBwdTile, 4>;
   constexpr int BN = kBwdTile;
   constexpr int NKB = BN / 32;
@@ -183,8 +186,21 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
     qf[cc] = row_ok ? *(const bf16x8 *)(Q + off) : bf16x8{};
     gf[cc] = row_ok ? *(const bf16x8 *)(dO + off) : bf16x8{};
   }
-  const float l2 = row_ok ? work[rows + (size_t)bh * N + qrow] : 0.f;
-  const float dd = row_ok ? work[(size_t)bh * N + qrow] : 0.f;
+  // D = sum_c dO[c] O[c] of this row (the two half-waves hold its two column halves) and
+  // L2 = L log2 e, also stored in `work` for the dK/dV kernel that runs next.
+  float dpart = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) {
+    const bf16x8 of = row_ok ? *(const bf16x8 *)(O + head + (size_t)qrow * D + 16 * cc + 8 * hh) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart = fmaf((float)gf[cc][e], (float)of[e], dpart);
+  }
+  const float dd = halves_sum(dpart);
+  const float l2 = row_ok ? L[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  if (row_ok && hh == 0) {
+    work[(size_t)bh * N + qrow] = dd;
+    work[rows + (size_t)bh * N + qrow] = l2;
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -794,15 +810,10 @@ hipError_t launch_bwd_bf16(int64_t BH, int N, hipStream_t s, const void *Q, cons
   const int ntiles = (N + kBwdRows - 1) / kBwdRows;
   // Both kernels stream two bf16 N x D matrices per head (K, V or Q, dO).
   const int group = head_group(BH, (int64_t)N * D * 2 * 2);
-  constexpr int prep_rows = 256 / (D / 8);
-  hipLaunchKernelGGL((fa_bwd_prep_kernel<bf16, D>), dim3((unsigned)((rows + prep_rows - 1) / prep_rows)), dim3(256), 0, s,
-                     (const bf16 *)O, (const bf16 *)dO, L, work, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(256), 0, s,
-                     (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
-                     (bf16 *)dQ, N, ntiles, rows, c, scale, group);
-  e = hipGetLastError();
+                     (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, (const bf16 *)O, L,
+                     work, (bf16 *)dQ, N, ntiles, rows, c, scale, group);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)(BH * ntiles)), dim3(512), 0, s,
                      (const bf16 *)Q, (const bf16 *)K, (const bf16 *)V, (const bf16 *)dO, work,
@@ -882,7 +893,8 @@ fa_status_t bwd_validate(const void *Q, const void *K, const void *V, const void
   return FA_OK;
 }
 
-// Enqueues the three kernels for validated arguments.
+// Enqueues the kernels for validated arguments (bf16: dQ then dK/dV; fp32:
+// preprocessing, dQ, dK/dV).
 fa_status_t bwd_launch(const void *Q, const void *K, const void *V, const void *O, const float *L,
                        const void *dO, void *dQ, void *dK, void *dV, float *work, int64_t B, int64_t H,
                        int64_t N, int64_t d, int causal, float scale, void *stream, int dtype) {
