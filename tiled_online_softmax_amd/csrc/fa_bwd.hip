@@ -238,6 +238,9 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_bf16_kernel(
       for (int cc = 0; cc < NCC; ++cc) {
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(ks, kb, cc), qf[cc], cc == 0 ? f32x16{} : s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta.row(vs, kb, cc), gf[cc], cc == 0 ? f32x16{} : dp[kb], 0, 0, 0);
+        // Each step's two operand reads stay next to its MFMAs: hoisting every
+        // read of the tile would spill at d = 128 (registers are full here).
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // P = exp2(S c - L2) (masked: 0) and dS = P (dP - D), as bf16 B operands.
