@@ -74,6 +74,13 @@ def test_too_long_sequence():
     assert call(N=(1 << 24) + 1) == fa.FA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("kw", [dict(B=1 << 32, H=1 << 32), dict(B=1 << 40), dict(H=(1 << 31) + 1)])
+def test_head_count_overflow(kw):
+    # B * H = 2^64 wraps to 0 in 64 bits: B and H are bounded before they are multiplied.
+    assert call(**kw) == fa.FA_ERR_UNSUPPORTED
+    assert call_spec(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_overlapping_output():
     # O overlaps K
     assert call(O=2 * A + 64) == fa.FA_ERR_INVALID_ARGUMENT
@@ -117,6 +124,11 @@ def test_bwd_unsupported(kw):
     assert call_bwd(**kw) == fa.FA_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("kw", [dict(B=1 << 32, H=1 << 32), dict(H=1 << 40)])
+def test_bwd_head_count_overflow(kw):
+    assert call_bwd(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_bwd_overlap_uses_element_size():
     # 64 x 64 fp32 tensors span 16 KiB: dQ 12 KiB after Q overlaps it (as bf16 it would not).
     assert call_bwd(dtype=fa.FA_DTYPE_F32, dQ=A + 12 * 1024) == fa.FA_ERR_INVALID_ARGUMENT
@@ -142,7 +154,8 @@ def call_bwd_noalloc(B=1, H=1, N=64, d=64, causal=0, scale=0.125, dtype=fa.FA_DT
 
 
 @pytest.mark.parametrize("kw", [dict(N=(1 << 20) + 1), dict(B=2, H=4, N=(1 << 17) + 1), dict(B=1 << 21),
-                                dict(B=1 << 40, H=1 << 40), dict(N=1 << 24)])
+                                dict(B=1 << 40, H=1 << 40), dict(N=1 << 24),
+                                dict(B=1 << 21, H=1 << 21, N=1 << 21)])  # 2 B H N = 2^64 wraps to 0
 def test_bwd_noalloc_size_limit(kw):
     assert call_bwd_noalloc(**kw) == fa.FA_ERR_SCRATCH_LIMIT
 
@@ -259,6 +272,9 @@ def test_jit_code_object_arguments():
     assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 96, 0, 1, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_jit_code_object(7, 64, 0, 1, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_INVALID_ARGUMENT
     assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 64, 0, 0, 1, 64, None, ctypes.byref(size)) == fa.FA_ERR_INVALID_ARGUMENT
+    # B * H = 2^64 would wrap to 0: rejected before anything is compiled.
+    assert lib.fa_jit_code_object(fa.FA_DTYPE_BF16, 64, 0, 1 << 32, 1 << 32, 64, None,
+                                  ctypes.byref(size)) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_attention_checks_rank():

@@ -867,6 +867,7 @@ fa_status_t bwd_validate(const void *Q, const void *K, const void *V, const void
   // bf16: d = 64, 128 (the 8-wave dK/dV tile loads need 8 KiB tiles); fp32 also d = 32.
   if (d != 64 && d != 128 && !(d == 32 && !bf)) return FA_ERR_UNSUPPORTED;
   if (N > (int64_t)1 << 24) return FA_ERR_UNSUPPORTED;
+  if (B > (int64_t)1 << 31 || H > (int64_t)1 << 31) return FA_ERR_UNSUPPORTED;  // B * H cannot overflow below
   const int64_t block_rows = bf ? kBwdRows : kF32Block;
   const int64_t ntiles = (N + block_rows - 1) / block_rows;
   if (B * H > ((int64_t)1 << 31) / ntiles - 1) return FA_ERR_UNSUPPORTED;
@@ -973,7 +974,8 @@ extern "C" fa_status_t fa_bwd_noalloc(const void *Q, const void *K, const void *
                                       int64_t B, int64_t H, int64_t N, int64_t d, int causal,
                                       float scale, void *stream, int dtype) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARGUMENT;
-  if (B > kBwdScratchFloats || H > kBwdScratchFloats || N > kBwdScratchFloats ||
+  // Each factor, then B * H, then the rows: no product below can overflow.
+  if (B > kBwdScratchFloats || H > kBwdScratchFloats || N > kBwdScratchFloats || B * H > kBwdScratchFloats ||
       2 * B * H * N > kBwdScratchFloats)
     return FA_ERR_SCRATCH_LIMIT;
   const fa_status_t st = bwd_validate(Q, K, V, O, L, dO, dQ, dK, dV, nullptr, false, B, H, N, d, scale, dtype);

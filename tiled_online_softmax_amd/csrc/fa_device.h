@@ -88,7 +88,7 @@ __device__ __forceinline__ void map_block(int bid, int nblocks, int n_qtiles, bo
 // time (groups of 4 MiB fetch less but run slower).
 inline int head_group(int64_t BH, int64_t tile_bytes) {
   constexpr int64_t kGroupBytes = (int64_t)8 << 20;
-  if (BH % kNumXcd != 0) return 0;
+  if (BH < kNumXcd || BH % kNumXcd != 0) return 0;
   const int64_t hpx = BH / kNumXcd;
   const int64_t fit = kGroupBytes / (tile_bytes > 0 ? tile_bytes : 1);
   int64_t g = hpx < 4096 ? hpx : 4096;

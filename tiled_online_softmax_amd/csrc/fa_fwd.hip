@@ -123,8 +123,10 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 bool supported_head_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // Row counts up to 2^24 keep every row index in 32 bits; the grid stays below 2^31.
+// B and H are bounded first, so that B * H cannot overflow.
 bool supported_sizes(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk) {
   if (Nq > (int64_t)1 << 24 || Nk > (int64_t)1 << 24) return false;
+  if (B > (int64_t)1 << 31 || H > (int64_t)1 << 31) return false;
   const int64_t block_rows = dtype == FA_DTYPE_BF16 ? kBf16Rows : kF32Rows;
   const int64_t n_qtiles = (Nq + block_rows - 1) / block_rows;
   return B * H <= ((int64_t)1 << 31) / n_qtiles - 1;
