@@ -127,7 +127,8 @@ fa_status_t fa_fwd_strided(const void *Q, const void *K, const void *V, void *O,
  * The first call for a (device, dtype, d, causal, B, H, N) compiles the
  * forward kernel source embedded in the library with hipRTC (for gfx950, with
  * the flags of the library's own build; about a second) and loads it on the
- * current device; later calls reuse it. Loaded kernels are kept until the
+ * stream's device (the current device for the null stream; the caller's
+ * current device is restored); later calls reuse it. Loaded kernels are kept until the
  * process ends. The cache is guarded by a mutex, so concurrent calls from
  * several threads are safe; a call that compiles blocks its thread meanwhile.
  * Returns FA_ERR_JIT if compiling or loading fails (nothing is enqueued).
@@ -197,8 +198,9 @@ fa_status_t fa_bwd(const void *Q, const void *K, const void *V, const void *O, c
  * 2*B*H*N-float workspace is a static array inside the library, one per GPU,
  * held until the process ends: at most 2^21 floats (8 MiB), so
  * B*H*N <= 2^20 rows (else FA_ERR_SCRATCH_LIMIT, nothing enqueued). The call
- * allocates nothing, on the host or the device. Every call on one GPU uses that
- * GPU's array; each call rewrites every entry it reads (per row: the sum over c
+ * allocates nothing, on the host or the device. Every call on one GPU (the
+ * stream's device; the current device for the null stream) uses that GPU's
+ * array; each call rewrites every entry it reads (per row: the sum over c
  * of dO*O, then L * log2 e) before reading it, so nothing carries over between
  * calls, but calls that overlap in time on one GPU (different streams, or
  * several host threads) race on the array and must be serialized by the

@@ -21,7 +21,7 @@ def fa():
     return tiled_online_softmax_amd
 
 
-def _case(fa, B, H, N, d, causal, dtype, seed):
+def _case(fa, B, H, N, d, causal, dtype, seed, side_stream=False):
     q, k, v = make_qkv(B, H, N, d, dtype, seed=seed)
     g = torch.Generator().manual_seed(seed + 1)
     do = torch.randn((B, H, N, d), generator=g).to(q.dtype)
@@ -32,7 +32,12 @@ def _case(fa, B, H, N, d, causal, dtype, seed):
     work = torch.empty(2 * B * H * N, dtype=torch.float32, device=DEV)
     fa.fa_bwd(qd, kd, vd, O, L, dod, *ref, work, B, H, N, d, causal, scale)
     got = [torch.full_like(qd, float("nan")) for _ in range(3)]
-    stream = torch.cuda.current_stream(DEV).cuda_stream
+    # On a stream of its own (a non-null handle: the library takes the GPU from the
+    # stream), ordered after the work above.
+    side = torch.cuda.Stream(DEV) if side_stream else None
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream(DEV))
+    stream = (side or torch.cuda.current_stream(DEV)).cuda_stream
     st = fa.raw_fa_bwd_noalloc(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), O.data_ptr(), L.data_ptr(),
                                dod.data_ptr(), *(t.data_ptr() for t in got), B, H, N, d, int(causal), scale,
                                stream, fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F32)
@@ -48,6 +53,11 @@ def test_noalloc_matches_fa_bwd(fa, dtype, d, causal):
     print(f"[no-alloc] {dtype} d={d} causal={causal}", flush=True)
     _case(fa, 2, 4, 1000, d, causal, dtype, seed=5100 + d)   # fills 16000 workspace floats
     _case(fa, 1, 2, 129, d, causal, dtype, seed=5200 + d)    # then a smaller problem on the same workspace
+
+
+def test_noalloc_on_side_stream(fa):
+    print("[no-alloc] bf16 d=128 causal on a side stream", flush=True)
+    _case(fa, 1, 4, 300, 128, True, "bf16", seed=5300, side_stream=True)
 
 
 def test_noalloc_size_limit(fa):

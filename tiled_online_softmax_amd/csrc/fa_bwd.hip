@@ -944,15 +944,18 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 float *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once fetched
 
-// The device address of the current device's copy of `scratch` (fetched on the
-// first call on that device, with it current), or null on failure.
-float *device_scratch() {
+// The device address of `scratch` on the device of `stream` (fetched on the
+// first call on that device, with that device current; the caller's current
+// device is restored), or null on failure.
+float *device_scratch(hipStream_t stream) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (stream_device(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (!g_scratch_ptr[dev]) {
     void *ptr = nullptr;
-    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    const hipError_t e =
+        on_device(dev, [&] { return hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess && ptr; });
+    if (e != hipSuccess) return nullptr;
     g_scratch_ptr[dev] = (float *)ptr;
   }
   return g_scratch_ptr[dev];
@@ -980,7 +983,7 @@ extern "C" fa_status_t fa_bwd_noalloc(const void *Q, const void *K, const void *
     return FA_ERR_SCRATCH_LIMIT;
   const fa_status_t st = bwd_validate(Q, K, V, O, L, dO, dQ, dK, dV, nullptr, false, B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
-  float *work = device_scratch();
+  float *work = device_scratch((hipStream_t)stream);
   if (!work) return FA_ERR_LAUNCH;
   return bwd_launch(Q, K, V, O, L, dO, dQ, dK, dV, work, B, H, N, d, causal, scale, stream, dtype);
 }

@@ -96,6 +96,26 @@ inline int head_group(int64_t BH, int64_t tile_bytes) {
   while (hpx % g != 0) --g;
   return (int)g;
 }
+
+// The device a launch on `stream` runs on: the stream's own device, or the
+// current device for the null stream.
+inline hipError_t stream_device(hipStream_t stream, int *device) {
+  if (!stream) return hipGetDevice(device);
+  return hipStreamGetDevice(stream, device);
+}
+
+// Runs f() with `device` current and restores the caller's current device;
+// hipErrorUnknown if f fails, else the first error of switching devices.
+template <typename F>
+hipError_t on_device(int device, F f) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+  const bool ok = f();
+  if (cur != device && (e = hipSetDevice(cur)) != hipSuccess) return e;
+  return ok ? hipSuccess : hipErrorUnknown;
+}
 #endif
 
 // Layout of a bf16 tile of BN rows x D columns staged in LDS (rows of K, V, Q

@@ -314,7 +314,7 @@ extern "C" fa_status_t fa_fwd_specialized(const void *Q, const void *K, const vo
   const fa_status_t st = validate_contiguous(Q, K, V, O, L, B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
   int device = 0;
-  if (hipGetDevice(&device) != hipSuccess) return FA_ERR_LAUNCH;
+  if (stream_device((hipStream_t)stream, &device) != hipSuccess) return FA_ERR_LAUNCH;
   JitKernel kern;
   {
     std::lock_guard<std::mutex> lock(g_jit_mutex);
@@ -324,12 +324,17 @@ extern "C" fa_status_t fa_fwd_specialized(const void *Q, const void *K, const vo
       std::string code, name;
       const fa_status_t cs = jit_compile(dtype, d, causal != 0, B, H, N, &code, &name);
       if (cs != FA_OK) return cs;
+      // Loaded on the stream's device, made current for the load.
       JitKernel k{};
-      if (hipModuleLoadData(&k.module, code.data()) != hipSuccess) return FA_ERR_JIT;
-      if (hipModuleGetFunction(&k.function, k.module, name.c_str()) != hipSuccess) {
-        (void)hipModuleUnload(k.module);  // already failing: the unload's status adds nothing
-        return FA_ERR_JIT;
-      }
+      const hipError_t e = on_device(device, [&] {
+        if (hipModuleLoadData(&k.module, code.data()) != hipSuccess) return false;
+        if (hipModuleGetFunction(&k.function, k.module, name.c_str()) != hipSuccess) {
+          (void)hipModuleUnload(k.module);  // already failing: the unload's status adds nothing
+          return false;
+        }
+        return true;
+      });
+      if (e != hipSuccess) return FA_ERR_JIT;
       it = g_jit_kernels.emplace(key, k).first;
     }
     kern = it->second;
