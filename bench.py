@@ -51,6 +51,34 @@ KERNEL_SOURCES = [os.path.join(ROOT, "tiled_online_softmax_amd", "csrc", f)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_kernel_{}_traffic.json")
 
 
+def device_info(fa) -> dict:
+    """The device as HIP reports it, beside the published peak the roofline uses: name,
+    architecture, compute units and peak engine clock, and the dense peaks they imply
+    (4096 bf16 / 256 fp32 matrix FLOP per clock and CU)."""
+    import ctypes
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", "").split(":")[0],
+            "compute_units": props.multi_processor_count}
+    # hipDeviceGetAttribute from the HIP runtime the library is linked against;
+    # attribute 5 is hipDeviceAttributeClockRate (peak engine clock, kHz).
+    try:
+        get = ctypes.CDLL(fa.LIB_PATH).hipDeviceGetAttribute
+    except (OSError, AttributeError):
+        return info
+    get.restype = ctypes.c_int
+    get.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    khz = ctypes.c_int(0)
+    if get(ctypes.byref(khz), 5, 0) == 0 and khz.value > 0:
+        ghz = khz.value / 1e6
+        info["peak_sclk_ghz"] = round(ghz, 3)
+        cu = props.multi_processor_count
+        info["implied_peak_tflops"] = {"bf16": round(cu * ghz * 4096 / 1e3, 1), "f32": round(cu * ghz * 256 / 1e3, 1)}
+    return info
+
+
 def source_digest() -> str:
     """sha256 over the forward kernel's source files, in a fixed order."""
     h = hashlib.sha256()
@@ -444,6 +472,7 @@ def main():
                          "why": "untimed steps before the warm-up steps: the GPU clock ramps up "
                                 "under sustained load"},
         "cpu_baseline": None,
+        "device": device_info(fa),
     }
     if bwd:
         rec["roofline"]["kernel_ms"]["covers"] = ("one fa_bwd call: dQ and dK/dV kernels" +
