@@ -82,3 +82,17 @@ def test_specialized_cache_reuses_kernel(fa):
         fa.forward_specialized(q, k, v)
     torch.cuda.synchronize()
     assert time.perf_counter() - t0 < 0.2
+
+
+def test_specialized_on_side_stream(fa):
+    """On a stream of its own (a non-null handle: the library loads the kernel on the stream's
+    device), ordered after the inputs' copies: bitwise equal to fa_fwd."""
+    q, k, v = (t.to(DEV) for t in make_qkv(2, 3, 777, 128, "bf16", seed=11))
+    ref_o, ref_l = fa.forward(q, k, v, causal=True, scale=default_scale(128))
+    side = torch.cuda.Stream(DEV)
+    O = torch.full_like(q, float("nan"))
+    L = torch.full((2, 3, 777), float("nan"), dtype=torch.float32, device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    fa.fa_fwd_specialized(q, k, v, O, L, 2, 3, 777, 128, True, default_scale(128), side)
+    torch.cuda.synchronize()
+    assert torch.equal(O, ref_o) and torch.equal(L, ref_l)
