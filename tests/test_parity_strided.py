@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import default_scale, make_qkv, make_qkv_cross
+from workloads import default_scale, make_qkv, make_qkv_cross, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -223,3 +223,59 @@ def test_strided_zero_batch_stride_inputs(fa):
     for b in range(B):
         for h in range(H):
             _compare(O[b:b + 1, h:h + 1], L[b:b + 1, h:h + 1], Oref, Lref, "bf16", f"broadcast ({b},{h})")
+
+
+# The largest sequence lengths the entry points accept (row indices stay in 32 bits; byte
+# offsets of rows past 2^24 x 64 elements do not).
+MAX_ROWS = 1 << 24
+
+
+def _max_rows_check(fa, Nq, Nk, causal, seed, n_sample):
+    d = 64
+    label = f"bf16 d={d} Nq={Nq} Nk={Nk} causal={causal}"
+    print(f"[parity-strided] generating {label}", flush=True)
+    q, k, v = make_qkv_cross(1, 1, Nq, Nk, d, "bf16", seed=seed)
+    scale = default_scale(d)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    O = torch.full_like(qd, float("nan"))
+    L = torch.full((1, 1, Nq), float("nan"), dtype=torch.float32, device=DEV)
+    print(f"[parity-strided] running {label}", flush=True)
+    fa.fa_fwd_strided(qd, kd, vd, O, L, causal, scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(L).all()), f"{label}: rows no workgroup wrote"
+    rows = sorted(set(sample_rows(Nq, n_sample, seed)) | {Nq - 1, Nq - 2, max(Nq - 129, 0), Nq // 2})
+    o, lse = O[:, :, rows].cpu(), L[:, :, rows].cpu()
+    del qd, kd, vd, O, L
+    # Rows are independent: the oracle takes the sampled query rows against every key. With the
+    # top-left causal mask, row i >= Nk - 1 sees every key; rows below Nk are compared as a
+    # causal prefix (local and global row indices agree there).
+    head = [r for r in rows if causal and r < Nk]
+    tail = [r for r in rows if r not in head]
+    Oref = np.empty((1, 1, len(rows), d))
+    Lref = np.empty((1, 1, len(rows)))
+    if tail:
+        ot, lt = oracle.attention_cross(q[:, :, tail].double().numpy(), k.double().numpy(), v.double().numpy(),
+                                        False, scale)
+        for j, r in enumerate(tail):
+            Oref[:, :, rows.index(r)], Lref[:, :, rows.index(r)] = ot[:, :, j], lt[:, :, j]
+    if head:
+        n = head[-1] + 1
+        oh, lh = oracle.attention_cross(q[:, :, :n].double().numpy(), k[:, :, :n].double().numpy(),
+                                        v[:, :, :n].double().numpy(), True, scale)
+        for r in head:
+            Oref[:, :, rows.index(r)], Lref[:, :, rows.index(r)] = oh[:, :, r], lh[:, :, r]
+    _compare(o, lse, Oref, Lref, "bf16", f"{label}, {len(rows)} sampled rows")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_max_query_rows(fa, causal):
+    """2^24 query rows (the largest Nq accepted) against 64 keys: every row is written, and
+    sampled rows up to the last one match the oracle."""
+    _max_rows_check(fa, MAX_ROWS, 64, causal, seed=77, n_sample=24)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_max_key_rows(fa, causal):
+    """256 query rows against 2^24 keys (the largest Nk accepted): sampled rows match the
+    oracle (non-causal: every key; causal: the top-left prefix)."""
+    _max_rows_check(fa, 256, MAX_ROWS, causal, seed=78, n_sample=8)
