@@ -156,6 +156,40 @@ def test_bwd_head_groups_per_xcd(fa, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_bwd_rows_past_2gib(fa, causal):
+    """2^24 rows (4096 heads of N = 4096 at d = 64, 2 GiB per matrix), so row addresses in the
+    second half of every matrix and of `work` lie past 2^31 bytes. Four seeded heads repeated
+    1024 times: dQ, dK and dV start as NaN and must come back finite, every head must equal
+    its base head bitwise (the same arithmetic wherever it lands), and the base heads must
+    match the oracle."""
+    base, reps, N, d = 4, 1024, 4096, 64
+    q, k, v, do = _inputs(1, base, N, d, seed=2300 + causal)
+    scale = default_scale(d)
+    dev = torch.device("cuda:0")
+    H = base * reps
+    print(f"[parity-bwd] {H} heads N={N} d={d} causal={causal}", flush=True)
+    qd, kd, vd, dod = (t.to(dev).repeat(1, reps, 1, 1) for t in (q, k, v, do))
+    O, L = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = (torch.full_like(qd, float("nan")) for _ in range(3))
+    work = torch.empty(2 * H * N, dtype=torch.float32, device=dev)
+    fa.fa_bwd(qd, kd, vd, O, L, dod, dq, dk, dv, work, 1, H, N, d, causal, scale)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), f"{name} has rows no workgroup wrote"
+        first = t[:, :base]
+        assert torch.equal(t.view(1, reps, base, N, d), first.unsqueeze(1).expand(1, reps, base, N, d)), \
+            f"{name}: a repeated head differs from its base head"
+    tol = TOL["bf16"]
+    Oc, Lc = O[:, :base].cpu(), L[:, :base].cpu()
+    ref, stored = stored_statistics_gradient(q, k, v, do, Oc, Lc, causal, scale)
+    for name, a, r, st in zip(("dQ", "dK", "dV"), (dq[:, :base], dk[:, :base], dv[:, :base]), ref, stored):
+        err = float(np.abs(a.double().cpu().numpy() - st).max())
+        bound = tol * max(1.0, float(np.abs(r).max()))
+        print(f"[parity-bwd] {H} heads causal={causal} {name} max|err|={err:.3e} (tol {bound:.3e})", flush=True)
+        assert err <= bound, f"{name} error {err} > {bound}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_bwd_long_sequence(fa, causal):
     """N = 4096 at d = 128: 32 key tiles per dQ workgroup, 64 query tiles per dK/dV workgroup."""
     q, k, v, do = _inputs(1, 2, 4096, 128, seed=2200 + causal)
