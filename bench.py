@@ -221,6 +221,55 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_per_dispatch": n * 4}), flush=True)
 
 
+def vs_sdpa(names, steps: int, warmup_seconds: float):
+    """fa_fwd beside torch's scaled_dot_product_attention (the fused attention PyTorch
+    ships for this GPU) on the given workloads: HIP events on the launch stream around
+    `steps` calls of each after a clock warm-up, and the largest difference between their
+    outputs. Context for the pages' comparison with SDPA; one JSON line per workload."""
+    import torch
+    import torch.nn.functional as F
+
+    import tiled_online_softmax_amd as fa
+    from workloads import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < warmup_seconds:
+            for _ in range(16):
+                fn()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    for name in names:
+        w = WORKLOADS[name]
+        if w.keys != w.N:
+            raise SystemExit(f"--vs-sdpa takes self-attention workloads ({name} has N_k != N)")
+        q, k, v = (t.to(dev) for t in w.make())
+        O = torch.empty_like(q)
+        L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        ms_fa = timed(lambda: fa.fa_fwd(q, k, v, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream))
+        ms_sdpa = timed(lambda: F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale))
+        ref = F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
+        fa.fa_fwd(q, k, v, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+        torch.cuda.synchronize()
+        flops = w.flops()
+        print(json.dumps({"vs_sdpa": name, "dtype": w.dtype, "steps": steps,
+                          "fa_fwd_us": round(ms_fa * 1e3, 2), "fa_fwd_tflops": round(flops / (ms_fa * 1e-3) / 1e12, 1),
+                          "sdpa_us": round(ms_sdpa * 1e3, 2), "sdpa_tflops": round(flops / (ms_sdpa * 1e-3) / 1e12, 1),
+                          "sdpa_over_fa": round(ms_sdpa / ms_fa, 2),
+                          "max_abs_diff_O": float((O.float() - ref.float()).abs().max()),
+                          "torch": torch.__version__}), flush=True)
+
+
 def small_sweep(reps: int):
     """The pages' small-shape sweep: per configuration, the median latency of one
     fa_fwd call, of torch's scaled_dot_product_attention and of the explicit
@@ -319,6 +368,9 @@ def main():
                     help="forward only: bshd stores Q, K, V, O as [B, N, H, d] and calls fa_fwd_strided")
     ap.add_argument("--specialize", action="store_true",
                     help="forward only: call fa_fwd_specialized (kernel compiled at run time for this shape)")
+    ap.add_argument("--vs-sdpa", action="store_true",
+                    help="instead of the benchmark, time fa_fwd beside torch's scaled_dot_product_attention on "
+                         "--workload (default: the bf16 workloads) and print one JSON line per workload")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark, run the small-shape fp32 sweep against torch SDPA")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -335,6 +387,11 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.vs_sdpa:
+        names = [args.workload] if args.workload else ["causal_bf16_b4h16n4096d128", "long_causal_bf16_h32n16384d64",
+                                                       "ragged_wide_logits_bf16_n1000"]
+        vs_sdpa(names, steps=max(args.steps, 1), warmup_seconds=args.warmup_seconds)
         return
     if args.sweep:
         small_sweep(reps=200)
