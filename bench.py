@@ -221,10 +221,11 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_per_dispatch": n * 4}), flush=True)
 
 
-def vs_sdpa(names, steps: int, warmup_seconds: float):
-    """fa_fwd beside torch's scaled_dot_product_attention (the fused attention PyTorch
-    ships for this GPU) on the given workloads: HIP events on the launch stream around
-    `steps` calls of each after a clock warm-up, and the largest difference between their
+def vs_sdpa(names, steps: int, warmup_seconds: float, bwd: bool = False):
+    """fa_fwd (or, with `bwd`, fa_bwd) beside torch's scaled_dot_product_attention (the
+    fused attention PyTorch ships for this GPU; its backward through autograd with the
+    graph kept) on the given workloads: HIP events on the launch stream around `steps`
+    calls of each after a clock warm-up, and the largest difference between their
     outputs. Context for the pages' comparison with SDPA; one JSON line per workload."""
     import torch
     import torch.nn.functional as F
@@ -256,6 +257,31 @@ def vs_sdpa(names, steps: int, warmup_seconds: float):
         q, k, v = (t.to(dev) for t in w.make())
         O = torch.empty_like(q)
         L = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        if bwd:
+            fa.fa_fwd(q, k, v, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+            g = torch.Generator().manual_seed(1000 + w.seed)
+            do = torch.randn((w.B, w.H, w.N, w.d), generator=g).to(q.dtype).to(dev)
+            grads = [torch.empty_like(q) for _ in range(3)]
+            work = torch.empty(2 * w.B * w.H * w.N, dtype=torch.float32, device=dev)
+            ms_fa = timed(lambda: fa.fa_bwd(q, k, v, O, L, do, *grads, work, w.B, w.H, w.N, w.d, w.causal,
+                                            w.scale, stream))
+            qg, kg, vg = (t.clone().requires_grad_(True) for t in (q, k, v))
+            out = F.scaled_dot_product_attention(qg, kg, vg, is_causal=w.causal, scale=w.scale)
+            ms_sdpa = timed(lambda: torch.autograd.grad(out, (qg, kg, vg), do, retain_graph=True))
+            ref = torch.autograd.grad(out, (qg, kg, vg), do, retain_graph=True)
+            fa.fa_bwd(q, k, v, O, L, do, *grads, work, w.B, w.H, w.N, w.d, w.causal, w.scale, stream)
+            torch.cuda.synchronize()
+            flops = 2 * w.flops()  # 8 d per pair: dV, dP, dQ, dK
+            print(json.dumps({"vs_sdpa": name, "pass": "bwd", "dtype": w.dtype, "steps": steps,
+                              "fa_bwd_us": round(ms_fa * 1e3, 2),
+                              "fa_bwd_tflops": round(flops / (ms_fa * 1e-3) / 1e12, 1),
+                              "sdpa_bwd_us": round(ms_sdpa * 1e3, 2),
+                              "sdpa_bwd_tflops": round(flops / (ms_sdpa * 1e-3) / 1e12, 1),
+                              "sdpa_over_fa": round(ms_sdpa / ms_fa, 2),
+                              "max_abs_diff_dQ_dK_dV": [float((a.float() - r.float()).abs().max())
+                                                        for a, r in zip(grads, ref)],
+                              "torch": torch.__version__}), flush=True)
+            continue
         ms_fa = timed(lambda: fa.fa_fwd(q, k, v, O, L, w.B, w.H, w.N, w.d, w.causal, w.scale, stream))
         ms_sdpa = timed(lambda: F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale))
         ref = F.scaled_dot_product_attention(q, k, v, is_causal=w.causal, scale=w.scale)
@@ -369,8 +395,9 @@ def main():
     ap.add_argument("--specialize", action="store_true",
                     help="forward only: call fa_fwd_specialized (kernel compiled at run time for this shape)")
     ap.add_argument("--vs-sdpa", action="store_true",
-                    help="instead of the benchmark, time fa_fwd beside torch's scaled_dot_product_attention on "
-                         "--workload (default: the bf16 workloads) and print one JSON line per workload")
+                    help="instead of the benchmark, time fa_fwd (with --pass bwd: fa_bwd) beside torch's "
+                         "scaled_dot_product_attention (its backward) on --workload (default: the large bf16 "
+                         "workloads) and print one JSON line per workload")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the benchmark, run the small-shape fp32 sweep against torch SDPA")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -389,9 +416,11 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.vs_sdpa:
-        names = [args.workload] if args.workload else ["causal_bf16_b4h16n4096d128", "long_causal_bf16_h32n16384d64",
-                                                       "ragged_wide_logits_bf16_n1000"]
-        vs_sdpa(names, steps=max(args.steps, 1), warmup_seconds=args.warmup_seconds)
+        names = ([args.workload] if args.workload else
+                 ["causal_bf16_b4h16n4096d128", "long_causal_bf16_h32n16384d64"] + (
+                     [] if args.which == "bwd" else ["ragged_wide_logits_bf16_n1000"]))
+        vs_sdpa(names, steps=max(args.steps if args.which == "fwd" else min(args.steps, 100), 1),
+                warmup_seconds=args.warmup_seconds, bwd=args.which == "bwd")
         return
     if args.sweep:
         small_sweep(reps=200)
