@@ -69,7 +69,8 @@ def one_query_attention(q, K, V, block_size: int, scale: float):
 
 
 def blockwise_attention(Q, K, V, q_block: int, k_block: int, causal: bool, scale: float,
-                        base2: bool = False, rescale_slack: float = 0.0):
+                        base2: bool = False, rescale_slack: float = 0.0,
+                        reference_lead: float = 0.0):
     """Tiled attention forward over one [N, d] head: returns (O [N, d], L [N]).
 
     Query rows are taken q_block at a time; for each, key/value rows are streamed
@@ -85,6 +86,12 @@ def blockwise_attention(Q, K, V, q_block: int, k_block: int, causal: bool, scale
     the rescale of l and u is skipped on such blocks. Because u and l always share
     one reference, u / l and m + log(l) are unchanged in exact arithmetic; slack 0
     is the plain recurrence. Exponentials are then bounded by exp(slack).
+
+    ``reference_lead`` >= 0 sets a reference that moves to the new maximum plus the
+    lead, so a row moves it again only after its maximum has grown by more than
+    lead + slack; the leading weights are then about exp(-lead). The same exact-
+    arithmetic argument applies (any reference gives the same u / l and m + log l);
+    lead 0 is the reference at the maximum.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -114,7 +121,7 @@ def blockwise_attention(Q, K, V, q_block: int, k_block: int, causal: bool, scale
                 s = np.where(kpos > qpos, -np.inf, s)
             bmax = s.max(axis=1, keepdims=True)
             grow = bmax > m + rescale_slack
-            m_next = np.where(grow, np.maximum(m, bmax), m)
+            m_next = np.where(grow, np.maximum(m, bmax) + reference_lead, m)
             with np.errstate(invalid="ignore"):
                 alpha = np.where(np.isneginf(m), 0.0, expf(m - m_next))
             w = expf(s - m_next)

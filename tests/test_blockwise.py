@@ -65,7 +65,7 @@ def test_tiled_16x16_on_single_head_workload():
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("blocks", [(16, 16), (128, 64), (64, 128), (32, 48)])
-@pytest.mark.parametrize("variant", ["plain", "base2", "base2_slack8"])
+@pytest.mark.parametrize("variant", ["plain", "base2", "base2_slack8", "base2_slack8_lead64"])
 def test_recurrence_on_ragged_wide_logits(causal, blocks, variant):
     """N = 1000 (not a multiple of any block), Q, K ~ N(0, 16): frequent max rescales."""
     w = WORKLOADS["ragged_wide_logits_bf16_n1000"]
@@ -73,9 +73,10 @@ def test_recurrence_on_ragged_wide_logits(causal, blocks, variant):
     Q, K, V = _f64(q[0, 0]), _f64(k[0, 0]), _f64(v[0, 0])
     O, L = oracle.attention(Q, K, V, causal, w.scale)
     base2 = variant != "plain"
-    slack = 8.0 if variant == "base2_slack8" else 0.0
+    slack = 8.0 if variant.startswith("base2_slack8") else 0.0
+    lead = 64.0 if variant.endswith("lead64") else 0.0
     Ob, Lb = blockwise.blockwise_attention(Q, K, V, blocks[0], blocks[1], causal, w.scale,
-                                           base2=base2, rescale_slack=slack)
+                                           base2=base2, rescale_slack=slack, reference_lead=lead)
     np.testing.assert_allclose(Ob, O, rtol=0, atol=1e-12)
     np.testing.assert_allclose(Lb, L, rtol=0, atol=1e-11)
 
@@ -91,6 +92,43 @@ def test_slack_keeps_probabilities_exact():
                                            rescale_slack=8.0)
     np.testing.assert_allclose(Ob, O, rtol=0, atol=1e-13)
     np.testing.assert_allclose(Lb, L, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("lead", [0.0, 64.0])
+def test_lead_keeps_probabilities_exact(lead):
+    """A reference set 64 (base 2) above the row maximum when it moves, with slack 8:
+    the probability rows are still exact, and so is L."""
+    r = np.random.default_rng(9)
+    n, d = 300, 16
+    Q, K, V = r.normal(size=(n, d)) * 4, r.normal(size=(n, d)) * 4, np.eye(n)[:, :d]
+    O, L = oracle.attention(Q, K, V, True, 0.25)
+    Ob, Lb = blockwise.blockwise_attention(Q, K, V, 32, 32, True, 0.25, base2=True,
+                                           rescale_slack=8.0, reference_lead=lead)
+    np.testing.assert_allclose(Ob, O, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Lb, L, rtol=0, atol=1e-11)
+
+
+def test_lead_moves_the_reference_less_often():
+    """On wide logits (Q, K ~ N(0, 16), d = 128) most 32-key blocks raise some row's
+    maximum past a reference at the maximum plus 8, and almost none past one set 64
+    above it: counted with the model's own grow rule, block by block."""
+    w = WORKLOADS["ragged_wide_logits_bf16_n1000"]
+    q, k, _ = make_qkv(1, 1, w.N, w.d, "bf16", w.seed, w.sigma_qk, w.sigma_v)
+    Q, K = _f64(q[0, 0]), _f64(k[0, 0])
+    s = (Q[:32] @ K.T) * w.scale * blockwise.LOG2E
+    moves = {}
+    for lead in (0.0, 64.0):
+        m = np.full(32, -np.inf)
+        count = 0
+        for k0 in range(32, w.N, 32):  # blocks after the first, which always moves it
+            if not np.isfinite(m).all():
+                m = s[:, :32].max(axis=1) + lead
+            bmax = s[:, k0:k0 + 32].max(axis=1)
+            grow = bmax > m + 8.0
+            count += int(grow.any())
+            m = np.where(grow, bmax + lead, m)
+        moves[lead] = count
+    assert moves[0.0] >= 10 and moves[64.0] <= 1, moves
 
 
 def test_causal_early_exit_equals_masking_every_block():

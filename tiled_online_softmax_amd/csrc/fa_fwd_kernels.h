@@ -78,7 +78,8 @@ namespace {
 // Software pipeline (per wave, iteration j):
 //   phase 1: MFMAs of S(j+1) = K(j+1) Q^T   |  VALU: P(j) = exp2(S(j) c - m), to bf16
 //   phase 2: MFMAs of O += V(j)^T P(j)^T     |  VALU: mask and row max of S(j+1), sum of P(j)
-//   then, if some row's maximum grew past the slack, rescale O and l (rare).
+//   then, if some row's maximum grew past the reference plus the slack,
+//   rescale O and l (rare: a moved reference sits 64 above the maximum).
 // K runs one tile ahead of V: iteration j reads K(j+1) and V(j); the loads
 // issued at its start fill K(j+2) and V(j+1), so every load has a whole
 // iteration to land before the barrier that publishes it.
@@ -139,6 +140,15 @@ constexpr int kOutOfRange = 1 << 30;
 // much (base-2 exponent) before the accumulators are rescaled: weights stay
 // below 2^8, and O/l and m + log2 l do not depend on the reference chosen.
 constexpr float kRescaleSlack = 8.0f;
+
+// bf16 kernel: a reference that moves is set this far above the row maximum
+// (base-2 exponent), so a row rescales only once its maximum has grown by more
+// than 64 + 8 since the reference last moved (with wide logits it otherwise
+// grows past the slack on most tiles). The weights stay below 2^8 as above; the
+// row's leading weights are about 2^-64, normal in fp32 and bf16. A weight
+// underflows to zero only for a key more than 62 below the row maximum, a
+// relative weight below 2^-62 per key (below 2^-38 for 2^24 keys).
+constexpr float kReferenceLead = 64.0f;
 
 // D < 32 (d = 16) runs on the layout of D = 32: the missing columns of the K
 // and V tiles are filled with zeros by out-of-range loads, Q's with zeros, and
@@ -296,13 +306,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
     return halves_max(mx);
   };
   // Move the reference maximum only when some row of the wave grew past the
-  // slack (always on the first tile, where m = -inf); rows that did not grow
-  // get alpha = 1.
+  // slack (always on the first tile, where m = -inf), to the new maximum plus
+  // the lead; rows that did not grow get alpha = 1.
   auto update_ref = [&](float mx) {
     const float mc = mx * c;
     const bool grow = mc > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? mc : m;
+      const float m_new = grow ? mc + kReferenceLead : m;
       const float alpha = exp2_fast(m - m_new);  // 0 while m is still -inf
       lsum *= alpha;
 #pragma unroll
