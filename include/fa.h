@@ -72,6 +72,14 @@ typedef enum {
  * differ in the last bits between launches with different B, H or N, because
  * small grids split each tile's keys between two waves (a different
  * summation order, within the same error bound).
+ *
+ * Value range (finite inputs; NaN and infinities propagate): with bf16 the
+ * output accumulators hold between about 2^-64 |v| and 2^8 N |v| (the softmax
+ * reference of a row sits up to 64 above its running maximum), so O keeps
+ * its relative precision for value magnitudes from about 2^-76 (through fp32
+ * denormals) up to 2^120 / N; below that O degrades in relative terms
+ * while its absolute error stays below the values' magnitude. fp32 keeps the
+ * reference at the row maximum: accumulators between |v| and 2^8 N |v|.
  */
 fa_status_t fa_fwd(const void *Q, const void *K, const void *V, void *O, float *L,
                    int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,

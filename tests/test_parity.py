@@ -280,6 +280,29 @@ def test_very_wide_logits(fa, causal):
            tol=(otol * sigma ** 2, ltol * sigma ** 2))
 
 
+@pytest.mark.parametrize("e", [-60, -30, 30, 60])
+@pytest.mark.parametrize("H", [2, 160])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_value_scale_range(fa, e, H, d, causal):
+    """V scaled by 2^e (exact in bf16), Q and K ~ N(0, 4^2): O scales by 2^e and L does not.
+    The bf16 kernel's accumulators hold about 2^-64 |v| after a reference move (the
+    reference sits 64 above the row maximum) and at most 2^8 N |v|, so V from 2^-60 to 2^60
+    keeps the unscaled case's relative precision. H = 2 runs the key-split grid, H = 160
+    the unsplit one."""
+    q, k, v = make_qkv(1, H, 300, d, "bf16", seed=48, sigma_qk=4.0)
+    vs = (v.double() * 2.0 ** e).to(torch.bfloat16)
+    assert torch.equal(vs.double() * 2.0 ** -e, v.double()), "power-of-two scaling is exact"
+    scale = default_scale(d)
+    O, L = _run(fa, q, k, vs, causal, scale)
+    Oref, Lref = oracle.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, scale)
+    Ob = O.double().cpu() * 2.0 ** -e
+    eo, el = _errors(Ob, L, Oref, Lref)
+    otol, ltol = TOL["bf16"]
+    print(f"[parity] V x 2^{e} H={H} d={d} causal={causal} max|dO|/2^{e}={eo:.3e} max|dL|={el:.3e}", flush=True)
+    assert eo <= otol and el <= ltol, (eo, el)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_uniform_closed_form(fa, dtype):
     """Q = 0: causal row i is the mean of value rows 0..i and L = log(i+1)."""
