@@ -76,10 +76,12 @@ namespace {
 //    a group pair land in 16 distinct slots.
 //
 // Software pipeline (per wave, iteration j):
-//   phase 1: MFMAs of S(j+1) = K(j+1) Q^T   |  VALU: P(j) = exp2(S(j) c - m), to bf16
-//   phase 2: MFMAs of O += V(j)^T P(j)^T     |  VALU: mask and row max of S(j+1), sum of P(j)
-//   then, if some row's maximum grew past the reference plus the slack,
-//   rescale O and l (rare: a moved reference sits 64 above the maximum).
+//   phase 1: MFMAs of S(j+1) = K(j+1) Q^T   |  VALU: P(j) = exp2(S(j) c - m) to bf16, its row sum
+//            and, only if some row's sum reached 2^8 (a row maximum grew past the
+//            reference plus the slack; rare, since a moved reference sits 64 above
+//            the maximum): the row maximum of S(j), the moved reference, O and l
+//            rescaled, P(j) and its sum formed again
+//   phase 2: MFMAs of O += V(j)^T P(j)^T     |  VALU: mask of S(j+1) (edge tiles)
 // K runs one tile ahead of V: iteration j reads K(j+1) and V(j); the loads
 // issued at its start fill K(j+2) and V(j+1), so every load has a whole
 // iteration to land before the barrier that publishes it.
@@ -322,20 +324,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
       m = m_new;
     }
   };
-  // P = exp2(S c - m) in place, and its bf16 copy as the B operand (P^T) of the
-  // second MFMA: key half mm of block kb is registers 8mm..8mm+7 of s[kb].
-  auto exponentiate = [&](f32x16 (&s)[NKW], bf16x8 (&pb)[NKW][2]) {
+  // P = exp2(S c - m) in bf16 as the B operand (P^T) of the second MFMA: key
+  // half mm of block kb is registers 8mm..8mm+7 of s[kb]. The scores stay as
+  // they are, in case the reference has to move and P be formed again.
+  auto exponentiate = [&](const f32x16 (&s)[NKW], bf16x8 (&pb)[NKW][2]) {
     const float mref = (m == -INFINITY) ? 0.f : m;  // no -inf - -inf
-#pragma unroll
-    for (int kb = 0; kb < NKW; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = exp2_fast(fmaf(s[kb][r], c, -mref));
 #pragma unroll
     for (int kb = 0; kb < NKW; ++kb)
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) pb[kb][mm][t8] = (bf16)s[kb][8 * mm + t8];
+        for (int t8 = 0; t8 < 8; ++t8) pb[kb][mm][t8] = (bf16)exp2_fast(fmaf(s[kb][8 * mm + t8], c, -mref));
   };
   // Adds to `acc` the row sum of the weights as they enter the second MFMA: the
   // bf16 values of P, two per v_dot2_f32_bf16 against (1, 1). Dividing by this
@@ -378,6 +377,25 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
       }
     }
   };
+  // The weights of a tile and their row sum, added to l. The row maximum is
+  // taken only when the reference may have to move: a row whose maximum grew
+  // past the reference plus the slack has a weight above 2^8, so the sum of
+  // its lane's weights reaches 2^8 (or is not finite). Then the wave takes the
+  // tile's row maxima, moves the references of the rows that grew (rescaling
+  // O and l) and forms P again; a lane whose sum reached 2^8 without a weight
+  // above 2^8 keeps its reference and gets the same P. Either way every weight
+  // that enters O and l is at most 2^8 (to the rounding of exp2 there), as when
+  // the maximum is taken on every tile.
+  auto weigh = [&](const f32x16 (&s)[NKW], bf16x8 (&pb)[NKW][2]) {
+    exponentiate(s, pb);
+    float ts = rowsum_into(pb, 0.f);
+    if (__builtin_amdgcn_ballot_w64(!(ts < 256.f))) {
+      update_ref(rowmax(s));
+      exponentiate(s, pb);
+      ts = rowsum_into(pb, 0.f);
+    }
+    lsum += ts;
+  };
   // All of this wave's loads issued so far have landed; after the barrier, so
   // have every wave's, and every wave is done with the previous iteration.
   auto publish = [&]() {
@@ -395,10 +413,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
     issue_v(t + 1);
     bf16x8 pb[NKW][2];
     scores(t + 1, s_nxt, std::false_type{});
-    exponentiate(s_cur, pb);
+    weigh(s_cur, pb);
     accumulate(t, pb, std::false_type{});
-    lsum = rowsum_into(pb, lsum);
-    update_ref(rowmax(s_nxt));
   };
   auto iteration_edge = [&](int t, f32x16 (&s_cur)[NKW], f32x16 (&s_nxt)[NKW]) {
     const bool has_next = t + 1 < nt;
@@ -407,13 +423,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fa_fwd_bf16_kernel(c
     if (has_next) issue_v(t + 1);
     bf16x8 pb[NKW][2];
     if (has_next) scores(t + 1, s_nxt, std::true_type{});
-    exponentiate(s_cur, pb);
+    weigh(s_cur, pb);
     accumulate(t, pb, std::true_type{});
-    lsum = rowsum_into(pb, lsum);
-    if (has_next) {
-      if (t + 1 >= nfull) mask(t + 1, s_nxt);
-      update_ref(rowmax(s_nxt));
-    }
+    if (has_next && t + 1 >= nfull) mask(t + 1, s_nxt);
   };
 
   f32x16 sa[NKW], sb[NKW];
