@@ -304,6 +304,25 @@ def test_value_scale_range(fa, e, H, d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H", [2, 160])
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_jumps(fa, dtype, H, causal):
+    """Scores that jump by hundreds (base 2) between key tiles: 0 for keys < 64, 362
+    (natural log) for keys 64..199, 724 from key 200 on. Against the reference kept
+    from the earlier keys the new weights overflow to infinity, so the kernels must move
+    the reference before those weights enter O and l (the bf16 kernel forms the tile's
+    weights again once their sum is not finite). H = 2 runs the key-split grid."""
+    N, d = 300, 128
+    _, _, v = make_qkv(1, H, N, d, dtype, seed=49)
+    q = torch.zeros(1, H, N, d, dtype=v.dtype)
+    k = torch.zeros(1, H, N, d, dtype=v.dtype)
+    q[..., 0] = 64.0
+    k[..., 64:200, 0] = 64.0
+    k[..., 200:, 0] = 128.0
+    _check(fa, q, k, v, causal, default_scale(d), dtype, label=f"score jumps {dtype} H={H} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_uniform_closed_form(fa, dtype):
     """Q = 0: causal row i is the mean of value rows 0..i and L = log(i+1)."""
     N, d = 333, 64
